@@ -1,0 +1,264 @@
+"""Benchmark: block-scaled FP8 linear-layer training pass on one MI355X.
+
+A step is one linear layer's full FP8 pass at the fused MLP gate+up shape of a ~2B decoder
+(X [8192, 2048] bf16 = 2 x 4096 tokens, W [12288, 2048], dY [8192, 12288]):
+  quantise X along K, quantise W by 128x128 tiles (+ transposed codes), fprop Y = X W^T,
+  quantise dY along N, dgrad dX = dY W, quantise dY and X along tokens, wgrad dW = dY^T X.
+Inputs are seeded synthetic tensors resident in HBM before timing starts.
+
+Printed (one JSON line): value = the three GEMMs' 2*M*N*K flops per step / step wall time
+(quantisers included), the fprop GEMM kernel against the FP8 MFMA roofline, per-kernel event
+timings, and the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--variant auto|mx|promote]
+                    [--no-cpu-baseline] [--no-configs]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FP8 block-scaled GEMM TFLOP/s and % of MI355X FP8 MFMA peak, 1 GPU"
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (AMD published figure, no sparsity)
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = "mlp_gateup_layer_step"
+KERNELS = ["quant_x_rows", "quant_w_tiles", "fprop_gemm", "quant_dy_rows", "dgrad_gemm", "quant_dy_cols",
+           "quant_x_cols", "wgrad_gemm"]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--variant", choices=["auto", "mx", "promote"], default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip timing the per-configuration GEMMs")
+    return ap.parse_args()
+
+
+def _dev_bf16(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def _alg_bytes(name, m, n, k):
+    """Algorithmic HBM bytes of one kernel launch (reads + writes, each byte once)."""
+    g = 128
+    if name in ("quant_x_rows", "quant_x_cols"):
+        rows, cols = m, k
+        return rows * cols * 2 + rows * cols + (rows * cols // g) * 4
+    if name in ("quant_dy_rows", "quant_dy_cols"):
+        return m * n * 2 + m * n + (m * n // g) * 4
+    if name == "quant_w_tiles":
+        return n * k * 2 + 2 * n * k + (n * k // (g * g)) * 4
+    if name == "fprop_gemm":
+        return m * k + n * k + m * n * 2 + (k // g) * m * 4 + (n // g) * (k // g) * 4
+    if name == "dgrad_gemm":
+        return m * n + k * n + m * k * 2 + (n // g) * m * 4 + (n // g) * (k // g) * 4
+    if name == "wgrad_gemm":
+        return n * m + k * m + n * k * 2 + (m // g) * n * 4 + (m // g) * k * 4
+    raise KeyError(name)
+
+
+def run_step_timed(step, steps, torch):
+    """Run `steps` steps with an event pair around every kernel launch (all on the current stream)."""
+    import fp8_block_scaled_pf8_amd._lib as L
+
+    st = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(steps)]
+    m, n, k, v = step.m, step.n, step.k, step.variant
+    s = st.cuda_stream
+    c = L.check
+    launches = [
+        lambda: c(L.pf8_quant_act_1x128(step.x.data_ptr(), m, k, k, L.PF8_ALONG_COLS, step.qx.data_ptr(), k,
+                                        step.sx.data_ptr(), m, s)),
+        lambda: c(L.pf8_quant_w_128x128(step.w.data_ptr(), n, k, k, step.qw.data_ptr(), k, step.qwt.data_ptr(), n,
+                                        step.sw.data_ptr(), k // 128, s)),
+        lambda: c(L.pf8_block_gemm_variant(v, L.PF8_FPROP, m, n, k, step.qx.data_ptr(), k, step.sx.data_ptr(), m,
+                                           step.qw.data_ptr(), k, step.sw.data_ptr(), k // 128, 1, step.y.data_ptr(),
+                                           n, s)),
+        lambda: c(L.pf8_quant_act_1x128(step.dy.data_ptr(), m, n, n, L.PF8_ALONG_COLS, step.qdy.data_ptr(), n,
+                                        step.sdy.data_ptr(), m, s)),
+        lambda: c(L.pf8_block_gemm_variant(v, L.PF8_DGRAD, m, k, n, step.qdy.data_ptr(), n, step.sdy.data_ptr(), m,
+                                           step.qwt.data_ptr(), n, step.sw.data_ptr(), 1, k // 128,
+                                           step.dx.data_ptr(), k, s)),
+        lambda: c(L.pf8_quant_act_1x128(step.dy.data_ptr(), m, n, n, L.PF8_ALONG_ROWS, step.qdyt.data_ptr(), m,
+                                        step.sdyt.data_ptr(), n, s)),
+        lambda: c(L.pf8_quant_act_1x128(step.x.data_ptr(), m, k, k, L.PF8_ALONG_ROWS, step.qxt.data_ptr(), m,
+                                        step.sxt.data_ptr(), k, s)),
+        lambda: c(L.pf8_block_gemm_variant(v, L.PF8_WGRAD, n, k, m, step.qdyt.data_ptr(), m, step.sdyt.data_ptr(), n,
+                                           step.qxt.data_ptr(), m, step.sxt.data_ptr(), 1, k, step.dw.data_ptr(), k,
+                                           s)),
+    ]
+    for i in range(steps):
+        e = evs[i]
+        e[0].record(st)
+        for j, fn in enumerate(launches):
+            fn()
+            e[j + 1].record(st)
+    return evs
+
+
+def time_config_gemms(pf8, torch, reps=20):
+    """Average kernel time of each configured GEMM (inputs quantised on the GPU first)."""
+    from workloads import WORKLOADS, generate
+
+    out = {}
+    for key in ["attn_fprop", "mlp_gateup_fprop", "mlp_down_fprop_dgrad", "wgrad"]:
+        wl = WORKLOADS[key]
+        t = generate(wl)
+        dev = {name: _dev_bf16(b, torch) for name, b in t.items()}
+        for layout, m, n, k in wl.gemms:
+            if layout == "fprop":
+                qx, sx = pf8.quant_act_1x128(dev["X"], "cols")
+                qw, _, sw = pf8.quant_w_128x128(dev["W"], transposed=False)
+                fn = lambda qx=qx, sx=sx, qw=qw, sw=sw: pf8.fprop(qx, sx, qw, sw, out=y)  # noqa: E731
+            elif layout == "dgrad":
+                qdy, sdy = pf8.quant_act_1x128(dev["dY"], "cols")
+                _, qwt, sw = pf8.quant_w_128x128(dev["W"])
+                fn = lambda qdy=qdy, sdy=sdy, qwt=qwt, sw=sw: pf8.dgrad(qdy, sdy, qwt, sw, out=y)  # noqa: E731
+            else:
+                qdyt, sdyt = pf8.quant_act_1x128(dev["dY"], "rows")
+                qxt, sxt = pf8.quant_act_1x128(dev["X"], "rows")
+                fn = lambda a=qdyt, sa=sdyt, b=qxt, sb=sxt: pf8.wgrad(a, sa, b, sb, out=y)  # noqa: E731
+            y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+            for _ in range(3):
+                fn()
+            st = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(reps):
+                fn()
+            e1.record(st)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            tf = 2.0 * m * n * k / (us * 1e-6) / 1e12
+            out[f"{key}:{layout}"] = {"m": m, "n": n, "k": k, "us": round(us, 2), "tflops": round(tf, 1),
+                                      "frac_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+        del dev
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(sample_tokens=2048):
+    """The oracle as it stands, on the first `sample_tokens` tokens of the same layer pass."""
+    import oracle
+    from workloads import generate
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    t = generate(WORKLOAD)
+    x, w, dy = t["X"][:sample_tokens], t["W"], t["dY"][:sample_tokens]
+    m, k = x.shape
+    n = w.shape[0]
+    t0 = time.perf_counter()
+    qx, sx = oracle.quant_act_1x128(x, "cols")
+    qw, qwt, sw = oracle.quant_w_128x128(w)
+    oracle.gemm_fprop(qx, sx, qw, sw)
+    qdy, sdy = oracle.quant_act_1x128(dy, "cols")
+    oracle.gemm_dgrad(qdy, sdy, qwt, sw)
+    qdyt, sdyt = oracle.quant_act_1x128(dy, "rows")
+    qxt, sxt = oracle.quant_act_1x128(x, "rows")
+    oracle.gemm_wgrad(qdyt, sdyt, qxt, sxt)
+    dt = time.perf_counter() - t0
+    flops = 3 * 2.0 * m * n * k
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"the same layer pass (all 7 steps, float64 oracle) on the first {m} of 8192 tokens: "
+                      f"X [{m},{k}], W [{n},{k}], dY [{m},{n}]; host cpus={os.cpu_count()} "
+                      f"affinity={len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); the path has no multi-GPU "
+              "mode: each GPU would run this same per-layer pass on its own micro-batch", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import fp8_block_scaled_pf8_amd as pf8
+    from workloads import WORKLOADS, generate
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    variant = {"auto": pf8.PF8_GEMM_AUTO, "mx": pf8.PF8_GEMM_MX_SCALED, "promote": pf8.PF8_GEMM_PROMOTE}[args.variant]
+    wl = WORKLOADS[WORKLOAD]
+    t = generate(wl)
+    x, w, dy = (_dev_bf16(t[nm], torch) for nm in ("X", "W", "dY"))
+    del t
+    step = pf8.LinearStep(x, w, dy, variant=variant)
+    m, n, k = step.m, step.n, step.k
+    print(f"# workload {WORKLOAD}: M={m} N={n} K={k}, variant={args.variant}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs = run_step_timed(step, args.steps, torch)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step_wall = wall * 1e3 / args.steps
+    # per-kernel averages from the events (same stream as the launches)
+    per = {name: 0.0 for name in KERNELS}
+    gpu_ms = 0.0
+    for e in evs:
+        for j, name in enumerate(KERNELS):
+            per[name] += e[j].elapsed_time(e[j + 1])
+        gpu_ms += e[0].elapsed_time(e[-1])
+    per = {kname: v / args.steps for kname, v in per.items()}
+    ms_step = gpu_ms / args.steps
+    flops = step.flops()
+    value = flops / (ms_step * 1e-3) / 1e12
+    kernels = {}
+    for name in KERNELS:
+        ms = per[name]
+        entry = {"us": round(ms * 1e3, 2)}
+        if name.endswith("gemm"):
+            tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+            entry.update(tflops=round(tf, 1), frac_peak=round(tf / PEAK_FP8_TFLOPS, 4))
+        else:
+            gbs = _alg_bytes(name, m, n, k) / (ms * 1e-3) / 1e9
+            entry.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+        kernels[name] = entry
+    fp_ms = per["fprop_gemm"]
+    achieved = 2.0 * m * n * k / (fp_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "fprop_gemm", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": 2 * m * n * k, "avg_launch_us": round(fp_ms * 1e3, 2)}
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": WORKLOAD, "m_tokens": m, "n": n, "k": k, "gemms": ["fprop", "dgrad", "wgrad"],
+                   "variant": args.variant, "title": wl.title},
+        "pct_of_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
+        "wall_ms_per_step": round(ms_step_wall, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_configs:
+        del step, x, w, dy
+        torch.cuda.empty_cache()
+        result["config_gemms"] = time_config_gemms(pf8, torch)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

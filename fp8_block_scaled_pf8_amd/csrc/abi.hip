@@ -1,0 +1,111 @@
+// C ABI of libpf8 (declared in include/pf8.h): host-side validation and dispatch.
+//
+// Every argument is checked before anything is enqueued; the checks need no GPU, so the library
+// loads and validates on a machine without one (and then reports PF8_ENODEV for valid calls).
+#include <stdint.h>
+
+#include "../../include/pf8.h"
+#include "pf8_launch.h"
+
+namespace {
+
+constexpr int64_t kGroup = 128;
+constexpr int64_t kMaxTilePitch = ((int64_t{1} << 31) - 1) / 256;  // 256 rows x pitch must fit a signed 32-bit offset
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int device_status() {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();  // clear the sticky error of a failed query
+    return PF8_ENODEV;
+  }
+  return PF8_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PF8_OK : PF8_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int pf8_abi_version(void) { return PF8_ABI_VERSION; }
+
+const char* pf8_strerror(int status) {
+  switch (status) {
+    case PF8_OK: return "ok";
+    case PF8_EINVAL: return "invalid argument (null pointer, unknown enum, non-positive dimension or leading dimension too small)";
+    case PF8_ESHAPE: return "unsupported shape (a grouped or tiled dimension is not a multiple of 128, col-mode cols not a multiple of 8, or a pitch too large)";
+    case PF8_EALIGN: return "misaligned buffer (base not 16-byte aligned or row pitch not a multiple of 16 bytes)";
+    case PF8_ENODEV: return "no HIP device available";
+    case PF8_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pf8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx, int axis, void* q, int64_t ldq,
+                        float* dscale, int64_t ld_s, void* hip_stream) {
+  if (x == nullptr || q == nullptr || dscale == nullptr) return PF8_EINVAL;
+  if (axis != PF8_ALONG_COLS && axis != PF8_ALONG_ROWS) return PF8_EINVAL;
+  if (rows <= 0 || cols <= 0) return PF8_EINVAL;
+  if (ldx < cols) return PF8_EINVAL;
+  if (axis == PF8_ALONG_COLS) {
+    if (cols % kGroup != 0) return PF8_ESHAPE;
+    if (ldq < cols || ld_s < rows) return PF8_EINVAL;
+  } else {
+    if (rows % kGroup != 0 || cols % 8 != 0) return PF8_ESHAPE;
+    if (ldq < rows || ld_s < cols) return PF8_EINVAL;
+  }
+  if (!aligned16(x) || !aligned16(q) || !aligned4(dscale) || (ldx * 2) % 16 != 0 || ldq % 16 != 0) return PF8_EALIGN;
+  // one grid row per 128-group of a row (row mode) or per 128-row band (col mode)
+  if ((axis == PF8_ALONG_COLS ? cols : rows) / kGroup > 65535) return PF8_ESHAPE;
+  if (int s = device_status(); s != PF8_OK) return s;
+  auto stream = static_cast<hipStream_t>(hip_stream);
+  const hipError_t e = axis == PF8_ALONG_COLS ? pf8::launch_quant_rows(x, rows, cols, ldx, q, ldq, dscale, ld_s, stream)
+                                              : pf8::launch_quant_cols(x, rows, cols, ldx, q, ldq, dscale, ld_s, stream);
+  return launch_status(e);
+}
+
+int pf8_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw, void* q, int64_t ldq, void* qt, int64_t ldqt,
+                        float* dscale, int64_t ld_s, void* hip_stream) {
+  if (w == nullptr || q == nullptr || dscale == nullptr) return PF8_EINVAL;
+  if (n <= 0 || k <= 0) return PF8_EINVAL;
+  if (n % kGroup != 0 || k % kGroup != 0) return PF8_ESHAPE;
+  if (ldw < k || ldq < k || ld_s < k / kGroup || (qt != nullptr && ldqt < n)) return PF8_EINVAL;
+  if (!aligned16(w) || !aligned16(q) || !aligned4(dscale) || (ldw * 2) % 16 != 0 || ldq % 16 != 0) return PF8_EALIGN;
+  if (qt != nullptr && (!aligned16(qt) || ldqt % 16 != 0)) return PF8_EALIGN;
+  if (n / kGroup > 65535) return PF8_ESHAPE;  // one grid row per 128-row tile band
+  if (int s = device_status(); s != PF8_OK) return s;
+  return launch_status(pf8::launch_quant_w(w, n, k, ldw, q, ldq, qt, ldqt, dscale, ld_s,
+                                           static_cast<hipStream_t>(hip_stream)));
+}
+
+int pf8_block_gemm_variant(int variant, int layout, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda,
+                           const float* a_dscale, int64_t ld_as, const void* b, int64_t ldb, const float* b_dscale,
+                           int64_t sb_n, int64_t sb_k, void* d, int64_t ldd, void* hip_stream) {
+  if (variant != PF8_GEMM_AUTO && variant != PF8_GEMM_MX_SCALED && variant != PF8_GEMM_PROMOTE) return PF8_EINVAL;
+  if (layout != PF8_FPROP && layout != PF8_DGRAD && layout != PF8_WGRAD) return PF8_EINVAL;
+  if (a == nullptr || b == nullptr || d == nullptr || a_dscale == nullptr || b_dscale == nullptr) return PF8_EINVAL;
+  if (m <= 0 || n <= 0 || k <= 0) return PF8_EINVAL;
+  if (k % kGroup != 0) return PF8_ESHAPE;
+  if (lda < k || ldb < k || ldd < n || ld_as < m || sb_n < 1 || sb_k < 1) return PF8_EINVAL;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(d) || !aligned4(a_dscale) || !aligned4(b_dscale)) return PF8_EALIGN;
+  if (lda % 16 != 0 || ldb % 16 != 0 || (ldd * 2) % 16 != 0) return PF8_EALIGN;
+  if (lda > kMaxTilePitch || ldb > kMaxTilePitch) return PF8_ESHAPE;
+  if ((m + 127) / 128 * ((n + 127) / 128) > (int64_t{1} << 31) - 1) return PF8_ESHAPE;
+  if (int s = device_status(); s != PF8_OK) return s;
+  pf8::GemmArgs args{m, n, k, static_cast<const uint8_t*>(a), lda, a_dscale, ld_as, static_cast<const uint8_t*>(b),
+                     ldb, b_dscale, sb_n, sb_k, static_cast<uint16_t*>(d), ldd};
+  const bool mx = variant != PF8_GEMM_PROMOTE;
+  return launch_status(pf8::launch_gemm(args, layout == PF8_WGRAD, mx, static_cast<hipStream_t>(hip_stream)));
+}
+
+int pf8_block_gemm(int layout, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const float* a_dscale,
+                   int64_t ld_as, const void* b, int64_t ldb, const float* b_dscale, int64_t sb_n, int64_t sb_k,
+                   void* d, int64_t ldd, void* hip_stream) {
+  return pf8_block_gemm_variant(PF8_GEMM_AUTO, layout, m, n, k, a, lda, a_dscale, ld_as, b, ldb, b_dscale, sb_n, sb_k,
+                                d, ldd, hip_stream);
+}
+
+}  // extern "C"

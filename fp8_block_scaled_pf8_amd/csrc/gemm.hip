@@ -1,0 +1,358 @@
+// Block-scaled FP8 GEMM for gfx950: D[i,j] = sum_kb sa(kb,i) sb(kb,j) sum_{k in kb} A[i,k] B[j,k].
+//
+// Method [paperlayer.ai summary, appendix C "Production Training Details", bullet "FP8
+// implementation pipeline"; paper.rainbus.top summary, 方法步骤详情 step (3)]: forward, data-gradient
+// and weight-gradient GEMMs take blockwise E4M3 operands; the product of the two block scales is
+// applied once per 128-wide K block and the result accumulates in FP32 and is written as BF16.
+//
+// Structure (one code path per variant, gfx950 only):
+//  * 256 threads = 4 waves in a 2x2 grid; the workgroup owns a BM x BN macro-tile of D and walks
+//    K in 128-wide blocks (one scale block per step).
+//  * A and B block tiles (BM x 128 and BN x 128 bytes) are fetched with 16-byte buffer loads
+//    (out-of-range rows of a ragged edge tile read as zero) one block ahead into registers and
+//    written to a double-buffered LDS ring; 16-byte chunk c of LDS row r sits at chunk
+//    c ^ (r & 7), so the MFMA operand reads of 8 consecutive rows hit distinct banks.
+//  * MX variant: v_mfma_scale_f32_32x32x64_f8f6f4. The scales are powers of two, so their
+//    exponent bytes are exact E8M0 scale operands and the matrix core applies sa*sb itself while
+//    accumulating in FP32 (the gfx950 counterpart of a block-scaled tensor-core path).
+//  * PROMOTE variant: v_mfma_f32_16x16x128_f8f6f4 covers one whole 128-wide scale block per
+//    instruction; it runs with a zero accumulator and the FP32 partial is folded into the
+//    running accumulator with one FMA by sa*sb per element.
+//  * The MFMA takes B as its first operand, so each lane ends up owning 4 consecutive output
+//    columns of one row: the epilogue converts to BF16 (RNE) and stores 8 bytes per lane.
+//  * Workgroup ids are remapped so each XCD (ids are dealt round-robin over 8) works on a
+//    contiguous range of tiles, walked in groups of 8 tile-rows for L2 reuse of A and B panels.
+#include "pf8_device.h"
+#include "pf8_launch.h"
+
+namespace pf8 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBufferFlags = 0x00020000;  // raw buffer resource word 3 for gfx9-family (dword data)
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 h = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+__device__ __forceinline__ int e8m0_of(float s) { return static_cast<int>(__float_as_uint(s) >> 23) & 0xFF; }
+
+__device__ __forceinline__ v8i lds_read32(const uint8_t* base, int off0, int off1) {
+  const v4i lo = *reinterpret_cast<const v4i*>(base + off0);
+  const v4i hi = *reinterpret_cast<const v4i*>(base + off1);
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Store 4 consecutive BF16 outputs of row m starting at column n (masked at the ragged edges).
+template <bool EDGE>
+__device__ __forceinline__ void store4(uint16_t* __restrict__ d, int64_t ldd, int64_t m, int64_t n, int64_t M,
+                                       int64_t N, float x0, float x1, float x2, float x3) {
+  const uint32_t w0 = pack_bf16x2(x0, x1), w1 = pack_bf16x2(x2, x3);
+  uint16_t* p = d + m * ldd + n;
+  if (!EDGE) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
+    return;
+  }
+  if (m >= M) return;
+  if (n + 3 < N) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
+  } else {
+    if (n < N) p[0] = static_cast<uint16_t>(w0);
+    if (n + 1 < N) p[1] = static_cast<uint16_t>(w0 >> 16);
+    if (n + 2 < N) p[2] = static_cast<uint16_t>(w1);
+  }
+}
+
+template <int BM, int BN, bool ROW_B, bool MX, bool EDGE>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+  constexpr int WM = BM / 2, WN = BN / 2;  // wave tile (2 x 2 waves)
+  constexpr int A_BYTES = BM * kGroup, B_BYTES = BN * kGroup, STAGE = A_BYTES + B_BYTES;
+  constexpr int A_LOADS = BM / 32, B_LOADS = BN / 32;  // 16-byte chunks per thread per K block
+  __shared__ __align__(16) uint8_t smem[2 * STAGE];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- tile scheduling: XCD-contiguous ranges, then groups of 8 tile-rows ----
+  int bid = blockIdx.x;
+  {
+    const int nb = gridDim.x, xcd = bid & 7, q = nb >> 3, rem = nb & 7;
+    bid = xcd * q + min(xcd, rem) + (bid >> 3);
+  }
+  constexpr int kGroupM = 8;
+  const int per_group = kGroupM * tiles_n;
+  const int grp = bid / per_group;
+  const int first_m = grp * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int in_grp = bid - grp * per_group;
+  const int tm = first_m + in_grp % gsize;
+  const int tn = in_grp / gsize;
+  const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * BN;
+  const int64_t M = p.m, N = p.n;
+  const int nk = static_cast<int>(p.k / kGroup);
+
+  // ---- global -> register loads ----
+  // Full tiles put the per-chunk row offset in the scalar offset (one lane offset for all loads).
+  // Edge tiles keep every row offset in the lane offset, so the buffer range check (sized to the
+  // valid rows) turns rows past the edge into zeros.
+  const int ld_row = t >> 3, ld_chunk = t & 7;
+  const int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
+  const int rows_a = EDGE ? static_cast<int>(min64(BM, M - m0)) : BM;
+  const int rows_b = EDGE ? static_cast<int>(min64(BN, N - n0)) : BN;
+  const __amdgpu_buffer_rsrc_t rsrc_a =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.a + m0 * p.lda), 0, rows_a * lda, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsrc_b =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.b + n0 * p.ldb), 0, rows_b * ldb, kBufferFlags);
+  const int voff_a = ld_row * lda + ld_chunk * 16;
+  const int voff_b = ld_row * ldb + ld_chunk * 16;
+  const int lds_w = ld_row * kGroup + ((ld_chunk ^ (ld_row & 7)) << 4);
+
+  v4i ra[A_LOADS], rb[B_LOADS];
+  auto gload = [&](int kb) {
+    const int kofs = kb * kGroup;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      const auto v = EDGE ? __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff_a + 32 * i * lda, kofs, 0)
+                          : __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff_a, 32 * i * lda + kofs, 0);
+      ra[i] = __builtin_bit_cast(v4i, v);
+    }
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+      const auto v = EDGE ? __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b + 32 * i * ldb, kofs, 0)
+                          : __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b, 32 * i * ldb + kofs, 0);
+      rb[i] = __builtin_bit_cast(v4i, v);
+    }
+  };
+  auto lds_store = [&](int stage) {
+    uint8_t* sa = smem + stage * STAGE;
+    uint8_t* sb = sa + A_BYTES;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) *reinterpret_cast<v4i*>(sa + lds_w + i * 32 * kGroup) = ra[i];
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) *reinterpret_cast<v4i*>(sb + lds_w + i * 32 * kGroup) = rb[i];
+  };
+  // scale of B's row j in K block kb
+  auto b_scale_idx = [&](int kb, int64_t j) -> int64_t {
+    if (EDGE) j = min64(j, N - 1);
+    return ROW_B ? static_cast<int64_t>(kb) * p.sb_k + j * p.sb_n : (j >> 7) * p.sb_n + static_cast<int64_t>(kb) * p.sb_k;
+  };
+  auto a_scale_idx = [&](int kb, int64_t i) -> int64_t {
+    if (EDGE) i = min64(i, M - 1);
+    return static_cast<int64_t>(kb) * p.ld_as + i;
+  };
+
+  if constexpr (MX) {
+    // ================= MX variant: 32x32x64 block-scaled MFMA =================
+    constexpr int TM = WM / 32, TN = WN / 32;
+    v16f acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // lane's scale rows: A row m0 + wm*WM + 32i + lane%32, B row n0 + wn*WN + 32j + lane%32
+    const int l32 = lane & 31, half = lane >> 5;
+    const int64_t a_row0 = m0 + wm * WM + l32, b_row0 = n0 + wn * WN + l32;
+    // raw fp32 scale bits; the E8M0 exponent byte (bits 23..30) is extracted where it is used,
+    // so the prefetch does not have to complete before this block's MFMAs are issued
+    uint32_t sa_raw[TM], sb_raw[TN], sa_nxt[TM], sb_nxt[TN];
+    auto load_scales = [&](int kb, uint32_t (&sa)[TM], uint32_t (&sb)[TN]) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sa[i] = __float_as_uint(p.a_dscale[a_scale_idx(kb, a_row0 + 32 * i)]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sb[j] = __float_as_uint(p.b_dscale[b_scale_idx(kb, b_row0 + 32 * j)]);
+    };
+    const int ra_row0 = wm * WM + l32, rb_row0 = wn * WN + l32;
+    const int sw = l32 & 7;  // (row & 7) for every fragment row this lane reads
+
+    gload(0);
+    load_scales(0, sa_raw, sb_raw);
+    lds_store(0);
+    __syncthreads();
+    for (int kb = 0; kb < nk; ++kb) {
+      const bool more = kb + 1 < nk;
+      if (more) {
+        gload(kb + 1);
+        load_scales(kb + 1, sa_nxt, sb_nxt);
+      }
+      int sae[TM], sbe[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sae[i] = static_cast<int>(sa_raw[i] >> 23);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sbe[j] = static_cast<int>(sb_raw[j] >> 23);
+      const uint8_t* sa = smem + (kb & 1) * STAGE;
+      const uint8_t* sb = sa + A_BYTES;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int c0 = ((4 * s + 2 * half) ^ sw) << 4, c1 = ((4 * s + 2 * half + 1) ^ sw) << 4;
+        v8i fa[TM], fb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int row = ra_row0 + 32 * i;
+          fa[i] = lds_read32(sa, row * kGroup + c0, row * kGroup + c1);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int row = rb_row0 + 32 * j;
+          fb[j] = lds_read32(sb, row * kGroup + c0, row * kGroup + c1);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0, sbe[j], 0,
+                                                                        sae[i]);
+      }
+      // keep the MFMAs ahead of the LDS refill, which has to wait for the prefetch to land
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) lds_store((kb + 1) & 1);
+      __syncthreads();
+      if (more) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sa_raw[i] = sa_nxt[i];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) sb_raw[j] = sb_nxt[j];
+      }
+    }
+    // epilogue: lane owns D[m][n .. n+3] with m = lane%32 of the tile, n = 8*(r/4) + 4*(lane/32)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t m = m0 + wm * WM + 32 * i + l32;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int64_t n = n0 + wn * WN + 32 * j + 8 * q4 + 4 * half;
+          store4<EDGE>(p.d, p.ldd, m, n, M, N, acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
+                       acc[i][j][4 * q4 + 3]);
+        }
+      }
+  } else {
+    // ================= PROMOTE variant: 16x16x128 MFMA per scale block + FP32 FMA =================
+    constexpr int TM = WM / 16, TN = WN / 16;
+    v4f acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int l16 = lane & 15, quarter = lane >> 4;
+    const int64_t a_row0 = m0 + wm * WM + l16;
+    const int64_t b_col0 = n0 + wn * WN + 4 * quarter;  // this lane's first output column in tile j = 0
+    const int ra_row0 = wm * WM + l16, rb_row0 = wn * WN + l16;
+    const int sw = l16 & 7;
+    const int c0 = ((2 * quarter) ^ sw) << 4, c1 = ((2 * quarter + 1) ^ sw) << 4;
+    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int NB = ROW_B ? 4 : 1;  // B scales per lane and 16-column tile
+    auto load_scales = [&](int kb, float (&sa_v)[TM], float (&sb_v)[TN][NB]) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sa_v[i] = p.a_dscale[a_scale_idx(kb, a_row0 + 16 * i)];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < NB; ++r) sb_v[j][r] = p.b_dscale[b_scale_idx(kb, b_col0 + 16 * j + r)];
+    };
+
+    float sa_v[TM], sb_v[TN][NB], sa_n[TM], sb_n[TN][NB];
+    gload(0);
+    load_scales(0, sa_v, sb_v);
+    lds_store(0);
+    __syncthreads();
+    for (int kb = 0; kb < nk; ++kb) {
+      const bool more = kb + 1 < nk;
+      if (more) {
+        gload(kb + 1);
+        load_scales(kb + 1, sa_n, sb_n);
+      }
+      const uint8_t* sa = smem + (kb & 1) * STAGE;
+      const uint8_t* sb = sa + A_BYTES;
+      v8i fa[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = ra_row0 + 16 * i;
+        fa[i] = lds_read32(sa, row * kGroup + c0, row * kGroup + c1);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int row = rb_row0 + 16 * j;
+        const v8i fb = lds_read32(sb, row * kGroup + c0, row * kGroup + c1);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[i], zero, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[i][j][r] = __builtin_fmaf(part[r], sa_v[i] * sb_v[j][ROW_B ? r : 0], acc[i][j][r]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) lds_store((kb + 1) & 1);
+      __syncthreads();
+      if (more) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sa_v[i] = sa_n[i];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < NB; ++r) sb_v[j][r] = sb_n[j][r];
+      }
+    }
+    // epilogue: lane owns D[m][n .. n+3], m = lane%16 of the tile, n = 4*(lane/16)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t m = m0 + wm * WM + 16 * i + l16;
+        const int64_t n = b_col0 + 16 * j;
+        store4<EDGE>(p.d, p.ldd, m, n, M, N, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
+  }
+}
+
+template <int BM, int BN, bool ROW_B, bool MX>
+static hipError_t launch_tile(const GemmArgs& args, hipStream_t stream) {
+  const int tiles_m = static_cast<int>((args.m + BM - 1) / BM);
+  const int tiles_n = static_cast<int>((args.n + BN - 1) / BN);
+  const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n)), block(256);
+  if (args.m % BM == 0 && args.n % BN == 0)
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, ROW_B, MX, false>), grid, block, 0, stream, args, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, ROW_B, MX, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, bool MX>
+static hipError_t launch_tile(const GemmArgs& args, bool row_b, hipStream_t stream) {
+  return row_b ? launch_tile<BM, BN, true, MX>(args, stream) : launch_tile<BM, BN, false, MX>(args, stream);
+}
+
+// Macro-tile choice (MX variant): 256x256 unless that leaves the 256 CUs badly under-filled, in
+// which case a 256x192 tile may even out the last wave (e.g. the 2048x6144 wgrad: 192 tiles of
+// 256x256 but exactly 256 of 256x192). Small problems use 128-row tiles. The PROMOTE variant keeps
+// an extra FP32 partial per MFMA in flight and uses 256x128 tiles to stay within registers.
+hipError_t launch_gemm(const GemmArgs& args, bool row_b_scale, bool mx, hipStream_t stream) {
+  if (!mx) {
+    if (args.m >= 256) return launch_tile<256, 128, false>(args, row_b_scale, stream);
+    return launch_tile<128, 128, false>(args, row_b_scale, stream);
+  }
+  auto fill = [&](int bm, int bn) {
+    const int64_t t = ((args.m + bm - 1) / bm) * ((args.n + bn - 1) / bn), waves = (t + 255) / 256;
+    return static_cast<double>(t) / static_cast<double>(waves * 256);
+  };
+  const double f256 = fill(256, 256), f192 = fill(256, 192);
+  if (args.m >= 256 && args.n >= 256 && f256 >= 0.9) return launch_tile<256, 256, true>(args, row_b_scale, stream);
+  if (args.m >= 256 && args.n >= 192 && f192 > f256) return launch_tile<256, 192, true>(args, row_b_scale, stream);
+  if (args.m >= 256 && args.n >= 256) return launch_tile<256, 256, true>(args, row_b_scale, stream);
+  if (args.m >= 256) return launch_tile<256, 128, true>(args, row_b_scale, stream);
+  return launch_tile<128, 128, true>(args, row_b_scale, stream);
+}
+
+}  // namespace pf8

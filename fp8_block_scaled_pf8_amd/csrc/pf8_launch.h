@@ -1,0 +1,34 @@
+// Host-side launchers of the libpf8 kernels (called by the C ABI after validation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pf8 {
+
+hipError_t launch_quant_rows(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q, int64_t ldq,
+                             float* dscale, int64_t ld_s, hipStream_t stream);
+hipError_t launch_quant_cols(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q, int64_t ldq,
+                             float* dscale, int64_t ld_s, hipStream_t stream);
+hipError_t launch_quant_w(const void* w, int64_t n, int64_t k, int64_t ldw, void* q, int64_t ldq, void* qt,
+                          int64_t ldqt, float* dscale, int64_t ld_s, hipStream_t stream);
+
+struct GemmArgs {
+  int64_t m, n, k;
+  const uint8_t* a;
+  int64_t lda;
+  const float* a_dscale;
+  int64_t ld_as;
+  const uint8_t* b;
+  int64_t ldb;
+  const float* b_dscale;
+  int64_t sb_n, sb_k;
+  uint16_t* d;
+  int64_t ldd;
+};
+
+// row_b_scale: B's scales are per (K-block, row) (wgrad) instead of per 128x128 tile.
+// mx: apply the scales inside the block-scaled MFMA; otherwise promote in FP32 registers.
+hipError_t launch_gemm(const GemmArgs& args, bool row_b_scale, bool mx, hipStream_t stream);
+
+}  // namespace pf8

@@ -1,0 +1,234 @@
+// Online power-of-two E4M3 quantisers for gfx950.
+//
+// Method [Puro-2B report; paper.rainbus.top summary, section "FP8 块级混合精度训练" and
+// 方法步骤详情 step (3); ta-paperlens explainer, 打ち手2 (report §3.2)]: one power-of-two scale per
+// 128 values along the reduction dimension for activations/gradients, per 128x128 tile for
+// weights, each computed from its own block when the tensor is quantised.
+//
+// All three kernels are HBM-bound streams (2 B read + ~1 B written per element): one read of the
+// input, block maxima reduced in registers / across lanes, then exact power-of-two scaling and
+// the hardware fp32 -> E4M3 RNE conversion.
+#include "pf8_device.h"
+#include "pf8_launch.h"
+
+namespace pf8 {
+
+// ---------------------------------------------------------------------------------------------
+// Row mode: a group is 128 consecutive elements of a row (16 lanes x 8 bf16).
+// Grid: x over row blocks of 16 * kRowUnroll rows, y over the cols / 128 groups of a row.
+// Lane slice s (16 lanes) of the workgroup handles rows r0 + s + 16 * u, u < kRowUnroll.
+constexpr int kRowUnroll = 4;
+constexpr int kRowsPerWG = 16 * kRowUnroll;
+
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx,
+                                                         uint8_t* __restrict__ q, int64_t ldq,
+                                                         float* __restrict__ dscale, int64_t ld_s) {
+  const int lane16 = threadIdx.x & 15;
+  const int slice = threadIdx.x >> 4;
+  const int64_t g = blockIdx.y;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kRowsPerWG + slice;
+  uint4 v[kRowUnroll];
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u) {
+    const int64_t r = r0 + 16 * u;
+    v[u] = make_uint4(0, 0, 0, 0);
+    if (r < rows) v[u] = *reinterpret_cast<const uint4*>(x + r * ldx + g * kGroup + lane16 * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u) {
+    const int64_t r = r0 + 16 * u;
+    // every lane of the 16-lane row takes part in the reduction (rows past the end hold zeros)
+    const uint32_t amax = row16_max(amax8_bits(v[u]));
+    const int e = block_exponent(amax);
+    const uint2 codes = quant8(v[u], pow2f(-e));
+    if (r < rows) {
+      *reinterpret_cast<uint2*>(q + r * ldq + g * kGroup + lane16 * 8) = codes;
+      if (lane16 == 0) dscale[g * ld_s + r] = pow2f(e);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Col mode: a group is 128 consecutive rows of one column; codes are written transposed
+// (q[c][r], rows contiguous). A workgroup quantises a 128-row x 64-column tile:
+//   thread t holds columns 8*(t%8) .. +7 of rows 4*(t/8) .. +3 (four 16-byte loads),
+//   column maxima are reduced over lanes (xor 8, 16, 32) and then over the 4 waves in LDS,
+//   codes go to an LDS tile [64 cols][128 rows] bytes and leave as 128-byte rows.
+// LDS 16-byte chunk ch of tile row c is stored at chunk ch ^ ((c >> 3) & 7) to spread banks.
+constexpr int kColTile = 64;
+
+__global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restrict__ x, int64_t cols, int64_t ldx,
+                                                         uint8_t* __restrict__ q, int64_t ldq,
+                                                         float* __restrict__ dscale, int64_t ld_s) {
+  __shared__ uint32_t red[4][kColTile];
+  __shared__ __align__(16) uint8_t tile[kColTile * kGroup];
+  const int t = threadIdx.x;
+  const int cc = t & 7;      // column chunk: columns 8*cc .. 8*cc+7 of the tile
+  const int rq = t >> 3;     // row quad: rows 4*rq .. 4*rq+3 of the group
+  const int wave = t >> 6;
+  const int64_t g = blockIdx.y;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kColTile;
+  const int64_t col = c0 + 8 * cc;
+  const bool col_ok = col < cols;  // cols % 8 == 0, so a chunk is all in or all out
+  uint4 v[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    v[p] = make_uint4(0, 0, 0, 0);
+    if (col_ok) v[p] = *reinterpret_cast<const uint4*>(x + (g * kGroup + 4 * rq + p) * ldx + col);
+  }
+  // per-column max of |x| over this thread's 4 rows; column j of the chunk lives in half (j&1) of word j/2
+  uint32_t m[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m[j] = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t w[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      m[2 * h] = max(m[2 * h], w[h] & 0x7FFFu);
+      m[2 * h + 1] = max(m[2 * h + 1], (w[h] >> 16) & 0x7FFFu);
+    }
+  }
+  // reduce over the 8 row quads of this wave (lanes differing in bits 3..5 share a column chunk)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t a = m[j];
+    a = max(a, static_cast<uint32_t>(__shfl_xor(static_cast<int>(a), 8)));
+    a = max(a, static_cast<uint32_t>(__shfl_xor(static_cast<int>(a), 16)));
+    a = max(a, static_cast<uint32_t>(__shfl_xor(static_cast<int>(a), 32)));
+    m[j] = a;
+  }
+  if ((t & 63) < 8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[wave][8 * cc + j] = m[j];
+  }
+  __syncthreads();
+  float inv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = 8 * cc + j;
+    const uint32_t a = max(max(red[0][c], red[1][c]), max(red[2][c], red[3][c]));
+    const int e = block_exponent(a);
+    inv[j] = pow2f(-e);
+    if (rq == 0 && col_ok) dscale[g * ld_s + c0 + c] = pow2f(e);
+  }
+  // quantise: for column j, the 4 codes of rows 4rq..4rq+3 form one little-endian dword
+  uint32_t colword[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) colword[j] = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t w[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int pair = cvt2_e4m3<false>(bf16_lo(w[h]) * inv[2 * h], bf16_hi(w[h]) * inv[2 * h + 1], 0);
+      colword[2 * h] |= (static_cast<uint32_t>(pair) & 0xFFu) << (8 * p);
+      colword[2 * h + 1] |= ((static_cast<uint32_t>(pair) >> 8) & 0xFFu) << (8 * p);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = 8 * cc + j;
+    const int ch = (rq >> 2) ^ ((c >> 3) & 7);
+    *reinterpret_cast<uint32_t*>(tile + c * kGroup + ch * 16 + (rq & 3) * 4) = colword[j];
+  }
+  __syncthreads();
+  // write out: 64 rows of 128 bytes; thread t handles chunk (t & 7) of tile rows (t >> 3) and (t >> 3) + 32
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = (t >> 3) + 32 * h;
+    const int ch = t & 7;
+    const uint4 val = *reinterpret_cast<const uint4*>(tile + c * kGroup + ((ch ^ ((c >> 3) & 7)) * 16));
+    if (c0 + c < cols) *reinterpret_cast<uint4*>(q + (c0 + c) * ldq + g * kGroup + ch * 16) = val;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Weight tiles: one workgroup per 128x128 tile.
+//   thread t holds the 8x8 block rows 8*(t/16) .. +7, columns 8*(t%16) .. +7 (eight 16-byte loads);
+//   the tile maximum is reduced over the wave and then over the 4 waves in LDS;
+//   codes go straight to q[n][k] (8 bytes per row per thread) and, when qt is requested,
+//   through an LDS tile [128 k][128 n] bytes to qt[k][n].
+__global__ __launch_bounds__(256) void quant_w_kernel(const uint16_t* __restrict__ w, int64_t ldw,
+                                                      uint8_t* __restrict__ q, int64_t ldq,
+                                                      uint8_t* __restrict__ qt, int64_t ldqt,
+                                                      float* __restrict__ dscale, int64_t ld_s) {
+  __shared__ uint32_t red[4];
+  __shared__ __align__(16) uint8_t tile[kGroup * kGroup];
+  const int t = threadIdx.x;
+  const int rb = t >> 4;  // row block: rows 8*rb .. 8*rb+7
+  const int cb = t & 15;  // col block: cols 8*cb .. 8*cb+7
+  const int64_t tn = blockIdx.y, tk = blockIdx.x;
+  const int64_t row0 = tn * kGroup + 8 * rb;
+  const int64_t col0 = tk * kGroup + 8 * cb;
+  uint4 v[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) v[p] = *reinterpret_cast<const uint4*>(w + (row0 + p) * ldw + col0);
+  uint32_t a = 0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) a = max(a, amax8_bits(v[p]));
+  a = wave_max(a);
+  if ((t & 63) == 0) red[t >> 6] = a;
+  __syncthreads();
+  a = max(max(red[0], red[1]), max(red[2], red[3]));
+  const int e = block_exponent(a);
+  const float inv = pow2f(-e);
+  if (t == 0) dscale[tn * ld_s + tk] = pow2f(e);
+  uint2 codes[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    codes[p] = quant8(v[p], inv);
+    *reinterpret_cast<uint2*>(q + (row0 + p) * ldq + col0) = codes[p];
+  }
+  if (qt == nullptr) return;  // uniform over the workgroup
+  // 8x8 byte transpose in registers: column j's 8 bytes (rows p = 0..7) form one 64-bit word
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const uint32_t word = (j < 4) ? codes[p].x : codes[p].y;
+      const uint32_t byte = (word >> (8 * (j & 3))) & 0xFFu;
+      if (p < 4) lo |= byte << (8 * p);
+      else hi |= byte << (8 * (p - 4));
+    }
+    const int c = 8 * cb + j;                 // tile row of qt (a column of w)
+    const int ch = (rb >> 1) ^ ((c >> 3) & 7);  // 16-byte chunk holding rows 8*rb .. 8*rb+7
+    *reinterpret_cast<uint2*>(tile + c * kGroup + ch * 16 + (rb & 1) * 8) = make_uint2(lo, hi);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int c = (t >> 3) + 32 * h;
+    const int ch = t & 7;
+    const uint4 val = *reinterpret_cast<const uint4*>(tile + c * kGroup + ((ch ^ ((c >> 3) & 7)) * 16));
+    *reinterpret_cast<uint4*>(qt + (tk * kGroup + c) * ldqt + tn * kGroup + ch * 16) = val;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+hipError_t launch_quant_rows(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q, int64_t ldq,
+                             float* dscale, int64_t ld_s, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((rows + kRowsPerWG - 1) / kRowsPerWG), static_cast<unsigned>(cols / kGroup));
+  hipLaunchKernelGGL(quant_rows_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(x), rows, ldx,
+                     static_cast<uint8_t*>(q), ldq, dscale, ld_s);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_cols(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q, int64_t ldq,
+                             float* dscale, int64_t ld_s, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((cols + kColTile - 1) / kColTile), static_cast<unsigned>(rows / kGroup));
+  hipLaunchKernelGGL(quant_cols_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(x), cols, ldx,
+                     static_cast<uint8_t*>(q), ldq, dscale, ld_s);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_w(const void* w, int64_t n, int64_t k, int64_t ldw, void* q, int64_t ldq, void* qt,
+                          int64_t ldqt, float* dscale, int64_t ld_s, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(k / kGroup), static_cast<unsigned>(n / kGroup));
+  hipLaunchKernelGGL(quant_w_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(w), ldw,
+                     static_cast<uint8_t*>(q), ldq, static_cast<uint8_t*>(qt), ldqt, dscale, ld_s);
+  return hipGetLastError();
+}
+
+}  // namespace pf8

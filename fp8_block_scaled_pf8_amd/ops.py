@@ -1,0 +1,167 @@
+"""Tensor-level wrappers over the libpf8 C ABI (PyTorch-ROCm supplies device memory and streams).
+
+Each wrapper validates dtypes/devices, allocates its outputs with torch and forwards raw pointers
+to the C entry point of the same purpose; every step of the computation runs in libpf8's HIP
+kernels. Codes are ``torch.uint8`` (OCP E4M3FN bit patterns; ``.view(torch.float8_e4m3fn)``
+reinterprets them), scales are float32 dequantisation multipliers.
+
+Layouts (reduction dimension contiguous for every GEMM operand):
+  quant_act_1x128(x [R, C], along="cols") -> q [R, C],  s [C/128, R]
+  quant_act_1x128(x [R, C], along="rows") -> q [C, R],  s [R/128, C]
+  quant_w_128x128(w [N, K])               -> q [N, K],  qt [K, N] (optional), s [N/128, K/128]
+  fprop(qx, sx, qw, sw)     -> Y  [M, N]   = X . W^T
+  dgrad(qdy, sdy, qwt, sw)  -> dX [M, K]   = dY . W      (qwt, sw from quant_w_128x128(W))
+  wgrad(qdyt, sdy, qxt, sx) -> dW [N, K]   = dY^T . X    (both from the along="rows" quantiser)
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib as L
+
+GROUP = 128
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check_2d(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a HIP device")
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} must have a contiguous last dimension")
+
+
+def quant_act_1x128(x: torch.Tensor, along: str = "cols") -> Tuple[torch.Tensor, torch.Tensor]:
+    """1x128 power-of-two E4M3 quantisation of activations / gradients."""
+    _check_2d(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    if along == "cols":
+        axis = L.PF8_ALONG_COLS
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        s = torch.empty((max(cols // GROUP, 1), rows), dtype=torch.float32, device=x.device)
+    elif along == "rows":
+        axis = L.PF8_ALONG_ROWS
+        q = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+        s = torch.empty((max(rows // GROUP, 1), cols), dtype=torch.float32, device=x.device)
+    else:
+        raise ValueError("along must be 'cols' or 'rows'")
+    L.check(L.pf8_quant_act_1x128(x.data_ptr(), rows, cols, x.stride(0), axis, q.data_ptr(), q.stride(0),
+                                  s.data_ptr(), s.stride(0), _stream(x)), "pf8_quant_act_1x128")
+    return q, s
+
+
+def quant_w_128x128(w: torch.Tensor, transposed: bool = True
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor], torch.Tensor]:
+    """128x128-tile power-of-two E4M3 quantisation of a weight; optionally also the transposed codes."""
+    _check_2d(w, torch.bfloat16, "w")
+    n, k = w.shape
+    q = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    qt = torch.empty((k, n), dtype=torch.uint8, device=w.device) if transposed else None
+    s = torch.empty((max(n // GROUP, 1), max(k // GROUP, 1)), dtype=torch.float32, device=w.device)
+    L.check(L.pf8_quant_w_128x128(w.data_ptr(), n, k, w.stride(0), q.data_ptr(), q.stride(0),
+                                  qt.data_ptr() if qt is not None else 0, qt.stride(0) if qt is not None else 0,
+                                  s.data_ptr(), s.stride(0), _stream(w)), "pf8_quant_w_128x128")
+    return q, qt, s
+
+
+def block_gemm(layout: int, a: torch.Tensor, a_dscale: torch.Tensor, b: torch.Tensor, b_dscale: torch.Tensor,
+               sb_n: int, sb_k: int, out: Optional[torch.Tensor] = None, variant: int = L.PF8_GEMM_AUTO
+               ) -> torch.Tensor:
+    """D[m, n] = sum_k deq(A)[m, k] deq(B)[n, k] in FP32, written as BF16 (see include/pf8.h)."""
+    _check_2d(a, torch.uint8, "a")
+    _check_2d(b, torch.uint8, "b")
+    _check_2d(a_dscale, torch.float32, "a_dscale")
+    if b_dscale.dtype != torch.float32 or not b_dscale.is_cuda:
+        raise TypeError("b_dscale must be a float32 device tensor")
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k:
+        raise ValueError(f"reduction dims differ: a {tuple(a.shape)}, b {tuple(b.shape)}")
+    if out is None:
+        # the C ABI wants 16-byte row pitches: pad the allocation, hand back the [m, n] view
+        pitch = (n + 7) // 8 * 8
+        out = torch.empty((m, pitch), dtype=torch.bfloat16, device=a.device)[:, :n]
+    _check_2d(out, torch.bfloat16, "out")
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out has the wrong shape")
+    L.check(L.pf8_block_gemm_variant(variant, layout, m, n, k, a.data_ptr(), a.stride(0), a_dscale.data_ptr(),
+                                     a_dscale.stride(0), b.data_ptr(), b.stride(0), b_dscale.data_ptr(), sb_n, sb_k,
+                                     out.data_ptr(), out.stride(0), _stream(a)), "pf8_block_gemm")
+    return out
+
+
+def fprop(qx, sx, qw, sw, out=None, variant: int = L.PF8_GEMM_AUTO) -> torch.Tensor:
+    """Y = X . W^T from row-mode X codes and W tile codes."""
+    return block_gemm(L.PF8_FPROP, qx, sx, qw, sw, sw.stride(0), 1, out, variant)
+
+
+def dgrad(qdy, sdy, qwt, sw, out=None, variant: int = L.PF8_GEMM_AUTO) -> torch.Tensor:
+    """dX = dY . W from row-mode dY codes (along N), W's transposed codes and W's tile grid."""
+    return block_gemm(L.PF8_DGRAD, qdy, sdy, qwt, sw, 1, sw.stride(0), out, variant)
+
+
+def wgrad(qdyt, sdy, qxt, sx, out=None, variant: int = L.PF8_GEMM_AUTO) -> torch.Tensor:
+    """dW = dY^T . X from col-mode (token-grouped) dY and X codes."""
+    return block_gemm(L.PF8_WGRAD, qdyt, sdy, qxt, sx, 1, sx.stride(0), out, variant)
+
+
+class LinearStep:
+    """One linear layer's FP8 training pass at a fixed shape, with every buffer preallocated.
+
+    forward:  X [M, K] -> codes along K, W [N, K] -> tile codes (+ transposed), Y = X . W^T
+    backward: dY [M, N] -> codes along N, dX = dY . W; dY and X -> codes along M, dW = dY^T . X
+    ``run`` enqueues the seven kernels on the current stream and allocates nothing.
+    """
+
+    def __init__(self, x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, variant: int = L.PF8_GEMM_AUTO):
+        for t, name in ((x, "x"), (w, "w"), (dy, "dy")):
+            _check_2d(t, torch.bfloat16, name)
+        (m, k), (n, k2), (m2, n2) = x.shape, w.shape, dy.shape
+        if k != k2 or m != m2 or n != n2:
+            raise ValueError("inconsistent shapes for X [M,K], W [N,K], dY [M,N]")
+        self.x, self.w, self.dy, self.variant = x, w, dy, variant
+        self.m, self.n, self.k = m, n, k
+        dev = x.device
+        u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+        e = lambda *s, dt=u8: torch.empty(s, dtype=dt, device=dev)  # noqa: E731
+        self.qx, self.sx = e(m, k), e(k // GROUP, m, dt=f32)
+        self.qw, self.qwt, self.sw = e(n, k), e(k, n), e(n // GROUP, k // GROUP, dt=f32)
+        self.qdy, self.sdy = e(m, n), e(n // GROUP, m, dt=f32)
+        self.qdyt, self.sdyt = e(n, m), e(m // GROUP, n, dt=f32)
+        self.qxt, self.sxt = e(k, m), e(m // GROUP, k, dt=f32)
+        self.y, self.dx, self.dw = e(m, n, dt=bf), e(m, k, dt=bf), e(n, k, dt=bf)
+
+    def flops(self) -> int:
+        return 3 * 2 * self.m * self.n * self.k
+
+    def run(self) -> None:
+        st = torch.cuda.current_stream(self.x.device).cuda_stream
+        m, n, k, v = self.m, self.n, self.k, self.variant
+        c = L.check
+        c(L.pf8_quant_act_1x128(self.x.data_ptr(), m, k, self.x.stride(0), L.PF8_ALONG_COLS, self.qx.data_ptr(), k,
+                                self.sx.data_ptr(), m, st), "quant X")
+        c(L.pf8_quant_w_128x128(self.w.data_ptr(), n, k, self.w.stride(0), self.qw.data_ptr(), k, self.qwt.data_ptr(),
+                                n, self.sw.data_ptr(), k // GROUP, st), "quant W")
+        c(L.pf8_block_gemm_variant(v, L.PF8_FPROP, m, n, k, self.qx.data_ptr(), k, self.sx.data_ptr(), m,
+                                   self.qw.data_ptr(), k, self.sw.data_ptr(), k // GROUP, 1, self.y.data_ptr(), n, st),
+          "fprop")
+        c(L.pf8_quant_act_1x128(self.dy.data_ptr(), m, n, self.dy.stride(0), L.PF8_ALONG_COLS, self.qdy.data_ptr(), n,
+                                self.sdy.data_ptr(), m, st), "quant dY")
+        c(L.pf8_block_gemm_variant(v, L.PF8_DGRAD, m, k, n, self.qdy.data_ptr(), n, self.sdy.data_ptr(), m,
+                                   self.qwt.data_ptr(), n, self.sw.data_ptr(), 1, k // GROUP, self.dx.data_ptr(), k,
+                                   st), "dgrad")
+        c(L.pf8_quant_act_1x128(self.dy.data_ptr(), m, n, self.dy.stride(0), L.PF8_ALONG_ROWS, self.qdyt.data_ptr(), m,
+                                self.sdyt.data_ptr(), n, st), "quant dY^T")
+        c(L.pf8_quant_act_1x128(self.x.data_ptr(), m, k, self.x.stride(0), L.PF8_ALONG_ROWS, self.qxt.data_ptr(), m,
+                                self.sxt.data_ptr(), k, st), "quant X^T")
+        c(L.pf8_block_gemm_variant(v, L.PF8_WGRAD, n, k, m, self.qdyt.data_ptr(), m, self.sdyt.data_ptr(), n,
+                                   self.qxt.data_ptr(), m, self.sxt.data_ptr(), 1, k, self.dw.data_ptr(), k, st),
+          "wgrad")

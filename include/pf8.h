@@ -1,0 +1,132 @@
+/*
+ * pf8.h - C ABI of libpf8: block-scaled FP8 (E4M3) linear-layer quantisers and GEMM for AMD MI355X (gfx950).
+ *
+ * The method [Puro-2B report; paper.rainbus.top summary, section "FP8 块级混合精度训练" and
+ * 方法步骤详情 step (3); ta-paperlens explainer, 打ち手2 (report §3.2); paperlayer.ai summary,
+ * appendix C "Production Training Details"]: the linear-layer GEMMs of training (forward,
+ * data-gradient, weight-gradient) run on E4M3 operands. Activations and gradients carry one
+ * power-of-two scale per 128 consecutive values along the GEMM reduction dimension, weights one
+ * per 128x128 tile; each scale is computed from its own block at quantisation time. The GEMM
+ * accumulates in FP32, applies the product of the two operands' block scales for every 128-wide
+ * K block, and writes BF16.
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer is a device pointer (HBM) unless stated otherwise; the caller allocates and
+ *    owns all buffers. The library never allocates, frees or synchronises and keeps no global
+ *    state: calls are thread-safe and re-entrant.
+ *  - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL = the null stream).
+ *  - Leading dimensions ("ld") are in elements of the array they describe.
+ *  - Every argument is validated on the host before anything is enqueued; on error nothing
+ *    runs and the call returns the status. A launch failure is reported as PF8_ELAUNCH.
+ *  - Scales are dequantisation multipliers: value = scale * decode(code). The quantisers write
+ *    exact powers of two 2^e, e in [-126, 120]; an all-zero block gets scale 1.
+ *  - E4M3 is the OCP E4M3FN encoding (bias 7, max 448, no infinities), rounded to nearest-even,
+ *    sign kept on zero. Inputs must be finite; NaN/Inf inputs give unspecified codes.
+ *  - Alignment: every code / bf16 array base is 16-byte aligned, and its row pitch
+ *    (ld * element size) is a multiple of 16 bytes. Scale arrays are 4-byte aligned.
+ */
+#ifndef PF8_H
+#define PF8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PF8_ABI_VERSION 1
+
+/* Status codes (int). */
+#define PF8_OK 0
+#define PF8_EINVAL 1  /* null pointer, unknown enum value, non-positive dimension, ld too small */
+#define PF8_ESHAPE 2  /* a grouped / tiled dimension is not a multiple of 128 (or 8, see below) */
+#define PF8_EALIGN 3  /* pointer not 16-byte aligned, or row pitch not a multiple of 16 bytes */
+#define PF8_ENODEV 4  /* no usable HIP device (the library loads and validates without one) */
+#define PF8_ELAUNCH 5 /* the kernel launch reported an error */
+
+/* Grouping axis of the activation / gradient quantiser. */
+#define PF8_ALONG_COLS 0 /* row mode: a group is 128 consecutive elements of one row */
+#define PF8_ALONG_ROWS 1 /* col mode: a group is 128 consecutive rows of one column; codes are written transposed */
+
+/* GEMM layouts. */
+#define PF8_FPROP 0 /* Y[M,N]  = X[M,K] . W[N,K]^T       B = W codes, one scale per 128x128 tile      */
+#define PF8_DGRAD 1 /* dX[M,K] = dY[M,N] . W[N,K]        B = W^T codes [K,N], W's tile scales via strides */
+#define PF8_WGRAD 2 /* dW[N,K] = dY[M,N]^T . X[M,K]      B = X^T codes [K,M], one scale per (128-block, row) */
+
+/* GEMM kernel variants (pf8_block_gemm_variant). */
+#define PF8_GEMM_AUTO 0      /* the fastest variant for the shape (what pf8_block_gemm runs) */
+#define PF8_GEMM_MX_SCALED 1 /* scales applied inside gfx950's block-scaled FP8 MFMA (E8M0 scale operands) */
+#define PF8_GEMM_PROMOTE 2   /* unscaled FP8 MFMA per 128-block, then FP32 scale-and-accumulate in registers */
+
+/*
+ * 1x128 activation / gradient quantiser [paper.rainbus.top summary, section "FP8 块级混合精度训练";
+ * ta-paperlens explainer, 打ち手2: activations and gradients get one scale per 128 elements along
+ * the reduction direction].
+ *
+ * x: bf16 [rows, cols], row pitch ldx (>= cols).
+ * axis = PF8_ALONG_COLS (row mode; e.g. fprop X along K, dgrad dY along N):
+ *     requires cols % 128 == 0 (rows arbitrary >= 1).
+ *     q:      u8 [rows, cols], row pitch ldq >= cols.
+ *     dscale: f32 [cols/128][rows], i.e. dscale[g * ld_s + r] for group g of row r; ld_s >= rows.
+ * axis = PF8_ALONG_ROWS (col mode; wgrad dY and X along the token dimension):
+ *     requires rows % 128 == 0 and cols % 8 == 0.
+ *     q:      u8 [cols, rows] (transposed, so the reduction dim is contiguous), row pitch ldq >= rows.
+ *     dscale: f32 [rows/128][cols], i.e. dscale[g * ld_s + c]; ld_s >= cols.
+ * Returns PF8_OK, PF8_EINVAL, PF8_ESHAPE, PF8_EALIGN, PF8_ENODEV or PF8_ELAUNCH.
+ */
+int pf8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                        void* q, int64_t ldq, float* dscale, int64_t ld_s, void* hip_stream);
+
+/*
+ * 128x128 weight-tile quantiser [paper.rainbus.top summary, section "FP8 块级混合精度训练" and
+ * 方法步骤详情 step (3): weights get one scale per 128x128 block].
+ *
+ * w:      bf16 [n, k], row pitch ldw >= k; requires n % 128 == 0 and k % 128 == 0.
+ * q:      u8 [n, k], row pitch ldq >= k.
+ * qt:     u8 [k, n] (the same codes transposed, for the data-gradient GEMM) or NULL; pitch ldqt >= n.
+ * dscale: f32 [n/128][k/128], i.e. dscale[tn * ld_s + tk]; ld_s >= k/128.
+ */
+int pf8_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw, void* q, int64_t ldq,
+                        void* qt, int64_t ldqt, float* dscale, int64_t ld_s, void* hip_stream);
+
+/*
+ * Block-scaled FP8 GEMM [paperlayer.ai summary, appendix C, bullet "FP8 implementation pipeline":
+ * the forward, data-gradient and weight-gradient GEMMs run on blockwise E4M3 operands].
+ *
+ *   D[i, j] = sum_{kb} sa(kb, i) * sb(kb, j) * sum_{k in block kb} decode(A[i, k]) * decode(B[j, k])
+ *
+ * with FP32 accumulation and a BF16 (round-to-nearest-even) result.
+ * m, n >= 1 (any value), k % 128 == 0.
+ * a: u8 [m, k] (pitch lda >= k), reduction dim contiguous.  a_dscale: f32, sa(kb, i) = a_dscale[kb * ld_as + i], ld_as >= m.
+ * b: u8 [n, k] (pitch ldb >= k), reduction dim contiguous.  b_dscale: f32, with
+ *     layout FPROP / DGRAD (tile scales): sb(kb, j) = b_dscale[(j / 128) * sb_n + kb * sb_k]
+ *         (fprop passes W's grid: sb_n = ld_s, sb_k = 1; dgrad passes the same grid transposed:
+ *          sb_n = 1, sb_k = ld_s);
+ *     layout WGRAD (1x128 row groups):  sb(kb, j) = b_dscale[kb * sb_k + j * sb_n]
+ *         (the col-mode quantiser's [K/128][n] array: sb_k = ld_s, sb_n = 1).
+ * d: bf16 [m, n], row pitch ldd >= n.
+ * The MX-scaled variant needs every scale to be an exact power of two in [2^-127, 2^127] (what the
+ * quantisers produce); PF8_GEMM_PROMOTE accepts any finite FP32 scales.
+ */
+int pf8_block_gemm(int layout, int64_t m, int64_t n, int64_t k,
+                   const void* a, int64_t lda, const float* a_dscale, int64_t ld_as,
+                   const void* b, int64_t ldb, const float* b_dscale, int64_t sb_n, int64_t sb_k,
+                   void* d, int64_t ldd, void* hip_stream);
+
+/* Same as pf8_block_gemm with an explicit kernel variant (PF8_GEMM_*); PF8_EINVAL for an unknown one. */
+int pf8_block_gemm_variant(int variant, int layout, int64_t m, int64_t n, int64_t k,
+                           const void* a, int64_t lda, const float* a_dscale, int64_t ld_as,
+                           const void* b, int64_t ldb, const float* b_dscale, int64_t sb_n, int64_t sb_k,
+                           void* d, int64_t ldd, void* hip_stream);
+
+/* Static, NUL-terminated description of a status code ("unknown status" for other values). */
+const char* pf8_strerror(int status);
+
+/* PF8_ABI_VERSION of the loaded library. */
+int pf8_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PF8_H */

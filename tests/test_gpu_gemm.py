@@ -1,0 +1,263 @@
+"""GPU block-scaled GEMM vs the CPU oracle (runs on an MI355X).
+
+Bar: every compared element satisfies |gpu - ref| <= 2^-7 |ref| + 1e-3 rms(ref), with ref the
+unrounded float64 oracle value on the same codes (the GPU quantisers' codes are checked
+bit-exact against the oracle's first). At the configured full sizes the oracle computes a
+seeded sample of output rows (spread over every row tile) against the complete columns.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_pf8_amd as pf8
+import oracle
+from workloads import WORKLOADS, f32_to_bf16_bits, generate
+from tests.gpu_helpers import DEV, bf16_bits, bf16_f64, f32, to_dev_bf16, to_dev_f32, to_dev_u8, u8
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = [pf8.PF8_GEMM_MX_SCALED, pf8.PF8_GEMM_PROMOTE]
+VNAME = {pf8.PF8_GEMM_MX_SCALED: "mx", pf8.PF8_GEMM_PROMOTE: "promote"}
+
+
+def _report(gpu_d, ref, what):
+    rep = oracle.gemm_tolerance_report(gpu_d, ref)
+    assert rep["violations"] == 0, f"{what}: {rep}"
+    # diagnostic, not the bar: most outputs round to the same bf16 as the float64 value
+    if rep["n"] >= 1000:
+        assert rep["frac_bit_equal_bf16"] > 0.95, f"{what}: {rep}"
+    return rep
+
+
+def _sample_rows(m, n_sample, seed):
+    if m <= n_sample:
+        return np.arange(m)
+    return np.sort(np.random.default_rng(seed).choice(m, n_sample, replace=False))
+
+
+def _quant_all_gpu(x_bits=None, w_bits=None, dy_bits=None):
+    """GPU quantisers on whichever inputs are given (each mode only where its shape allows it)."""
+    out = {}
+    for name, bits in (("x", x_bits), ("dy", dy_bits)):
+        if bits is None:
+            continue
+        t = to_dev_bf16(bits)
+        if bits.shape[1] % 128 == 0:
+            out["q" + name], out["s" + name] = pf8.quant_act_1x128(t, "cols")
+        if bits.shape[0] % 128 == 0 and bits.shape[1] % 8 == 0:
+            out["q" + name + "t"], out["s" + name + "t"] = pf8.quant_act_1x128(t, "rows")
+    if w_bits is not None:
+        out["qw"], out["qwt"], out["sw"] = pf8.quant_w_128x128(to_dev_bf16(w_bits))
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: VNAME[v])
+@pytest.mark.parametrize("key", ["tiny_fprop", "attn_fprop", "mlp_gateup_fprop", "mlp_down_fprop_dgrad"])
+def test_fprop_workloads(key, variant):
+    t = generate(key, only=["X", "W"])
+    g = _quant_all_gpu(x_bits=t["X"], w_bits=t["W"])
+    qx, sx = oracle.quant_act_1x128(t["X"], "cols")
+    qw, qwt, sw = oracle.quant_w_128x128(t["W"])
+    assert np.array_equal(u8(g["qx"]), qx) and np.array_equal(u8(g["qw"]), qw)
+    y = pf8.fprop(g["qx"], g["sx"], g["qw"], g["sw"], variant=variant)
+    torch.cuda.synchronize()
+    rows = _sample_rows(qx.shape[0], 384, 11)
+    ref = oracle.gemm_fprop(qx[rows], sx[:, rows], qw, sw)
+    _report(bf16_f64(y)[rows], ref, f"{key} fprop")
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: VNAME[v])
+def test_dgrad_workload(variant):
+    t = generate("mlp_down_fprop_dgrad", only=["W", "dY"])
+    g = _quant_all_gpu(w_bits=t["W"], dy_bits=t["dY"])
+    qdy, sdy = oracle.quant_act_1x128(t["dY"], "cols")
+    qw, qwt, sw = oracle.quant_w_128x128(t["W"])
+    assert np.array_equal(u8(g["qdy"]), qdy) and np.array_equal(u8(g["qwt"]), qwt)
+    dx = pf8.dgrad(g["qdy"], g["sdy"], g["qwt"], g["sw"], variant=variant)
+    torch.cuda.synchronize()
+    rows = _sample_rows(qdy.shape[0], 384, 12)
+    ref = oracle.gemm_dgrad(qdy[rows], sdy[:, rows], qwt, sw)
+    _report(bf16_f64(dx)[rows], ref, "dgrad")
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: VNAME[v])
+def test_wgrad_workload(variant):
+    t = generate("wgrad")
+    g = _quant_all_gpu(x_bits=t["X"], dy_bits=t["dY"])
+    qdyt, sdy = oracle.quant_act_1x128(t["dY"], "rows")
+    qxt, sx = oracle.quant_act_1x128(t["X"], "rows")
+    assert np.array_equal(u8(g["qdyt"]), qdyt) and np.array_equal(u8(g["qxt"]), qxt)
+    dw = pf8.wgrad(g["qdyt"], g["sdyt"], g["qxt"], g["sxt"], variant=variant)
+    torch.cuda.synchronize()
+    rows = _sample_rows(qdyt.shape[0], 256, 13)
+    ref = oracle.gemm_wgrad(qdyt[rows], sdy[:, rows], qxt, sx)
+    _report(bf16_f64(dw)[rows], ref, "wgrad")
+
+
+def _rand_bits(shape, seed, sigma=1.0):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(shape) * sigma).astype(np.float32)
+    x.reshape(-1)[rng.choice(x.size, max(1, x.size // 200), replace=False)] *= 50
+    return f32_to_bf16_bits(x)
+
+
+SHAPES = [(1, 1, 128), (1, 130, 256), (3, 5, 128), (300, 200, 384), (257, 129, 256), (513, 777, 640),
+          (256, 384, 512), (640, 448, 256), (129, 1000, 128)]
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: VNAME[v])
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_ragged_shapes_all_layouts(m, n, k, variant):
+    """Ragged M and N (any value) with K a multiple of 128: all three layouts, full outputs."""
+    # fprop: A = X [m, k] row codes, B = W [n', k] tile codes with n' padded to 128 rows
+    xb = _rand_bits((m, k), m * 7 + n)
+    n_pad = (n + 127) // 128 * 128
+    wb = _rand_bits((n_pad, k), n * 3 + k, 0.02)
+    qx, sx = oracle.quant_act_1x128(xb, "cols")
+    qw, qwt, sw = oracle.quant_w_128x128(wb)
+    d = pf8.fprop(to_dev_u8(qx), to_dev_f32(sx), to_dev_u8(qw[:n]), to_dev_f32(sw), variant=variant)
+    torch.cuda.synchronize()
+    _report(bf16_f64(d), oracle.gemm_fprop(qx, sx, qw[:n], sw), f"fprop {m}x{n}x{k}")
+    # dgrad: A = dY [m, k'] along its columns; B = W^T codes [n, k'] (first n rows), W tile grid [k'/128, *]
+    wb2 = _rand_bits((k, n_pad), k + n, 0.01)  # W [Nw = k, Kw = n_pad]
+    q2, qt2, sw2 = oracle.quant_w_128x128(wb2)
+    dyb = _rand_bits((m, k), m + 5, 1e-3)
+    qdy, sdy = oracle.quant_act_1x128(dyb, "cols")
+    d = pf8.dgrad(to_dev_u8(qdy), to_dev_f32(sdy), to_dev_u8(qt2[:n]), to_dev_f32(sw2), variant=variant)
+    torch.cuda.synchronize()
+    _report(bf16_f64(d), oracle.gemm_dgrad(qdy, sdy, qt2[:n], sw2), f"dgrad {m}x{n}x{k}")
+    # wgrad: A = dY^T codes [m, k] grouped along k (tokens), B = X^T codes [n, k]
+    dyt = _rand_bits((k, m + (-m % 8)), m + 11, 1e-3)
+    xt = _rand_bits((k, n + (-n % 8)), n + 13)
+    qa, sa = oracle.quant_act_1x128(dyt, "rows")
+    qb, sb = oracle.quant_act_1x128(xt, "rows")
+    d = pf8.wgrad(to_dev_u8(qa[:m]), to_dev_f32(sa), to_dev_u8(qb[:n]), to_dev_f32(sb), variant=variant)
+    torch.cuda.synchronize()
+    _report(bf16_f64(d), oracle.gemm_wgrad(qa[:m], sa[:, :m], qb[:n], sb[:, :n]), f"wgrad {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: VNAME[v])
+def test_identity_weight_reproduces_dequantised_input(variant):
+    xb = _rand_bits((512, 512), 21)
+    qx, sx = oracle.quant_act_1x128(xb, "cols")
+    eye = f32_to_bf16_bits(np.eye(512, dtype=np.float32))
+    g = _quant_all_gpu(w_bits=eye)
+    y = pf8.fprop(to_dev_u8(qx), to_dev_f32(sx), g["qw"], g["sw"], variant=variant)
+    dx = pf8.dgrad(to_dev_u8(qx), to_dev_f32(sx), g["qwt"], g["sw"], variant=variant)
+    torch.cuda.synchronize()
+    deq = oracle.decode_e4m3(qx) * np.repeat(sx.T.astype(np.float64), 128, 1) + 0.0
+    want = f32_to_bf16_bits(deq.astype(np.float32))
+    assert np.array_equal(bf16_bits(y), want)
+    assert np.array_equal(bf16_bits(dx), want)
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: VNAME[v])
+def test_one_hot_gradient_selects_rows_in_wgrad(variant):
+    xb = _rand_bits((256, 384), 22)
+    pick = np.array([0, 255, 17, 128, 129, 64, 200, 3])
+    dy = np.zeros((256, 8), np.float32)
+    dy[pick, np.arange(8)] = 1.0
+    g = _quant_all_gpu(x_bits=xb, dy_bits=f32_to_bf16_bits(dy))
+    dw = pf8.wgrad(g["qdyt"], g["sdyt"], g["qxt"], g["sxt"], variant=variant)
+    torch.cuda.synchronize()
+    qxt, sxt = oracle.quant_act_1x128(xb, "rows")
+    deq_x = (oracle.decode_e4m3(qxt) * np.repeat(sxt.T.astype(np.float64), 128, 1)).T + 0.0
+    assert np.array_equal(bf16_bits(dw), f32_to_bf16_bits(deq_x[pick].astype(np.float32)))
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: VNAME[v])
+def test_small_integer_block_is_exact(variant):
+    """Single and multi-block GEMMs whose FP32 sums are exact: the GPU must equal the exact value."""
+    rng = np.random.default_rng(5)
+    ints = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0xB8, 0xC0, 0xC4, 0xC8], np.uint8)  # 0, +-1, +-2, +-3, +-4
+    # products are multiples of 2^-4 below 2^8 and |sums| stay below 2^18: every partial sum is an fp32 value
+    for m, n, k in [(64, 64, 128), (256, 256, 512), (300, 260, 1024)]:
+        qa = rng.choice(ints, size=(m, k))
+        qb = rng.choice(ints, size=(n, k))
+        sa = np.ldexp(1.0, rng.integers(-2, 3, size=(k // 128, m))).astype(np.float32)
+        sb = np.ldexp(1.0, rng.integers(-2, 3, size=((n + 127) // 128, k // 128))).astype(np.float32)
+        d = pf8.fprop(to_dev_u8(qa), to_dev_f32(sa), to_dev_u8(qb), to_dev_f32(sb), variant=variant)
+        torch.cuda.synchronize()
+        ref = oracle.gemm_fprop(qa, sa, qb, sb)  # exact: small integers times powers of two
+        want = oracle.bf16_round_from_f64(ref)
+        assert np.array_equal(bf16_bits(d), want), f"{m}x{n}x{k}"
+
+
+def test_variants_agree_and_repeat_bitwise():
+    t = generate("tiny_fprop")
+    g = _quant_all_gpu(x_bits=t["X"], w_bits=t["W"])
+    outs = [pf8.fprop(g["qx"], g["sx"], g["qw"], g["sw"], variant=pf8.PF8_GEMM_MX_SCALED) for _ in range(3)]
+    auto = pf8.fprop(g["qx"], g["sx"], g["qw"], g["sw"])
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    assert torch.equal(auto, outs[0])
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: VNAME[v])
+def test_padded_output_and_strided_operands(variant):
+    """lda > k, ld_as > m and ldd > n: bytes outside D's [m, n] window stay untouched."""
+    m, n, k = 200, 300, 256
+    xb = _rand_bits((m, k), 31)
+    wb = _rand_bits((384, k), 32, 0.02)
+    qx, sx = oracle.quant_act_1x128(xb, "cols")
+    qw, _, sw = oracle.quant_w_128x128(wb)
+    a = np.zeros((m, 272), np.uint8)
+    a[:, :k] = qx
+    sa = np.zeros((2, 208), np.float32)
+    sa[:, :m] = sx
+    a_d, sa_d = to_dev_u8(a), to_dev_f32(sa)
+    b_d, sb_d = to_dev_u8(qw), to_dev_f32(sw)
+    canary = 0x7FC1  # a bf16 NaN pattern nothing writes
+    d = torch.full((m + 3, 312), canary, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    pf8._lib.check(pf8.pf8_block_gemm_variant(variant, pf8.PF8_FPROP, m, n, k, a_d.data_ptr(), 272, sa_d.data_ptr(),
+                                              208, b_d.data_ptr(), k, sb_d.data_ptr(), sw.shape[1], 1, d.data_ptr(),
+                                              312, torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    bits = bf16_bits(d)
+    assert np.all(bits[:m, n:] == canary) and np.all(bits[m:, :] == canary)
+    got = (bits[:m, :n].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    _report(got, oracle.gemm_fprop(qx, sx, qw[:n], sw), "strided")
+
+
+def test_linear_step_matches_oracle():
+    """The whole layer pass used by the benchmark (7 launches) on the tiny shape."""
+    t = generate("tiny_fprop")
+    dyb = _rand_bits((256, 384), 41, 1e-3)
+    step = pf8.LinearStep(to_dev_bf16(t["X"]), to_dev_bf16(t["W"]), to_dev_bf16(dyb))
+    step.run()
+    torch.cuda.synchronize()
+    qx, sx = oracle.quant_act_1x128(t["X"], "cols")
+    qw, qwt, sw = oracle.quant_w_128x128(t["W"])
+    qdy, sdy = oracle.quant_act_1x128(dyb, "cols")
+    qdyt, sdyt = oracle.quant_act_1x128(dyb, "rows")
+    qxt, sxt = oracle.quant_act_1x128(t["X"], "rows")
+    _report(bf16_f64(step.y), oracle.gemm_fprop(qx, sx, qw, sw), "step fprop")
+    _report(bf16_f64(step.dx), oracle.gemm_dgrad(qdy, sdy, qwt, sw), "step dgrad")
+    _report(bf16_f64(step.dw), oracle.gemm_wgrad(qdyt, sdyt, qxt, sxt), "step wgrad")
+
+
+def test_layer_step_workload_sampled():
+    """The benchmark's gate+up layer pass at full size: sampled codes and outputs against the oracle.
+
+    Row-mode groups live in one row and col-mode groups in one column, so the oracle quantises
+    just the sampled rows / columns of dY."""
+    wl = WORKLOADS["mlp_gateup_layer_step"]
+    t = generate(wl)
+    step = pf8.LinearStep(to_dev_bf16(t["X"]), to_dev_bf16(t["W"]), to_dev_bf16(t["dY"]))
+    step.run()
+    torch.cuda.synchronize()
+    rows = _sample_rows(8192, 128, 51)
+    qx, sx = oracle.quant_act_1x128(t["X"], "cols")
+    qw, qwt, sw = oracle.quant_w_128x128(t["W"])
+    assert np.array_equal(u8(step.qx), qx) and np.array_equal(u8(step.qw), qw) and np.array_equal(u8(step.qwt), qwt)
+    _report(bf16_f64(step.y)[rows], oracle.gemm_fprop(qx[rows], sx[:, rows], qw, sw), "layer fprop")
+    qdy, sdy = oracle.quant_act_1x128(np.ascontiguousarray(t["dY"][rows]), "cols")
+    assert np.array_equal(u8(step.qdy)[rows], qdy) and np.array_equal(f32(step.sdy)[:, rows], sdy)
+    _report(bf16_f64(step.dx)[rows], oracle.gemm_dgrad(qdy, sdy, qwt, sw), "layer dgrad")
+    cols = _sample_rows(12288, 128, 52)
+    qdyt, sdyt = oracle.quant_act_1x128(np.ascontiguousarray(t["dY"][:, cols]), "rows")
+    qxt, sxt = oracle.quant_act_1x128(t["X"], "rows")
+    assert np.array_equal(u8(step.qdyt)[cols], qdyt) and np.array_equal(u8(step.qxt), qxt)
+    _report(bf16_f64(step.dw)[cols], oracle.gemm_wgrad(qdyt, sdyt, qxt, sxt), "layer wgrad")

@@ -1,0 +1,145 @@
+"""GPU quantisers vs the CPU oracle: codes and scales bit-exact (runs on an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_pf8_amd as pf8
+import oracle
+from workloads import f32_to_bf16_bits, generate
+from tests.gpu_helpers import DEV, f32, to_dev_bf16, u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_act(bits, along):
+    q, s = pf8.quant_act_1x128(to_dev_bf16(bits), along)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_act_1x128(bits, along)
+    gq, gs = u8(q), f32(s)
+    assert gq.shape == q_ref.shape and gs.shape == s_ref.shape
+    bad = np.count_nonzero(gq != q_ref)
+    assert bad == 0, f"{bad} code mismatches, first at {np.argwhere(gq != q_ref)[:5].tolist()}"
+    assert np.array_equal(gs.view(np.uint32), s_ref.view(np.uint32))
+
+
+def _check_w(bits):
+    q, qt, s = pf8.quant_w_128x128(to_dev_bf16(bits))
+    torch.cuda.synchronize()
+    q_ref, qt_ref, s_ref = oracle.quant_w_128x128(bits)
+    assert np.array_equal(u8(q), q_ref)
+    assert np.array_equal(u8(qt), qt_ref)
+    assert np.array_equal(f32(s).view(np.uint32), s_ref.view(np.uint32))
+
+
+def _every_bf16_pattern(rows_of=512):
+    """All finite bf16 patterns, shuffled into rows so each 128-group has a different maximum."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = (bits.astype(np.uint32) << 16).view(np.float32)
+    bits = bits[np.isfinite(f)]
+    rng = np.random.default_rng(0)
+    bits = rng.permutation(bits)
+    n = (len(bits) // rows_of) * rows_of
+    return bits[:n].reshape(-1, rows_of)
+
+
+def test_row_mode_every_bf16_pattern():
+    _check_act(_every_bf16_pattern(512), "cols")
+
+
+def test_col_mode_every_bf16_pattern():
+    b = _every_bf16_pattern(512)  # [127, 512] -> take 128 rows x 512 worth by tiling
+    b = np.concatenate([b, b[:1]], 0)[:128]
+    _check_act(np.ascontiguousarray(b), "rows")
+    _check_act(np.ascontiguousarray(b[:, ::-1]), "rows")
+
+
+def test_weight_every_bf16_pattern():
+    b = _every_bf16_pattern(128)[:384]
+    _check_w(np.ascontiguousarray(b.reshape(384, 128)))
+
+
+def test_special_values():
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((256, 512)) * 0.3).astype(np.float32)
+    x[0, :128] = 0.0                        # all-zero group -> e = 0
+    x[1, :128] = -0.0                       # negative zeros keep their sign
+    x[2, :128] = np.float32(2.0 ** -133)    # smallest subnormal: clamp e = -126
+    x[3, :128] = np.float32(-3.3895314e38)  # largest finite bf16 magnitude: e = 120
+    x[4, 128:256] = np.float32(448.0)       # exactly 448 * 2^0
+    x[5, 128:256] = 450.0                   # just above: e = 1
+    x[6, 256:384] *= np.float32(1e-30)
+    x[7, :] = np.float32(2.0 ** -140)       # rounds to bf16 zero / tiny
+    bits = f32_to_bf16_bits(x)
+    _check_act(bits, "cols")
+    _check_act(bits, "rows")
+    _check_w(bits)
+
+
+@pytest.mark.parametrize("key,name", [("tiny_fprop", "X"), ("attn_fprop", "X"), ("mlp_down_fprop_dgrad", "X"),
+                                      ("mlp_down_fprop_dgrad", "dY")])
+def test_row_mode_workloads(key, name):
+    _check_act(generate(key, only=[name])[name], "cols")
+
+
+@pytest.mark.parametrize("key,name", [("wgrad", "dY"), ("wgrad", "X"), ("tiny_fprop", "X")])
+def test_col_mode_workloads(key, name):
+    _check_act(generate(key, only=[name])[name], "rows")
+
+
+@pytest.mark.parametrize("key", ["tiny_fprop", "attn_fprop", "mlp_gateup_fprop", "mlp_down_fprop_dgrad"])
+def test_weight_workloads(key):
+    _check_w(generate(key, only=["W"])["W"])
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 128), (3, 256), (63, 128), (65, 384), (1000, 640)])
+def test_row_mode_ragged_rows(rows, cols):
+    rng = np.random.default_rng(rows)
+    _check_act(f32_to_bf16_bits(rng.standard_normal((rows, cols)).astype(np.float32)), "cols")
+
+
+@pytest.mark.parametrize("rows,cols", [(128, 8), (128, 72), (256, 136), (384, 2056)])
+def test_col_mode_ragged_cols(rows, cols):
+    rng = np.random.default_rng(cols)
+    _check_act(f32_to_bf16_bits(rng.standard_normal((rows, cols)).astype(np.float32)), "rows")
+
+
+def test_strided_inputs_and_untouched_padding():
+    """Leading dimensions larger than the rows: padding bytes of q and dscale stay untouched."""
+    rng = np.random.default_rng(9)
+    bits = f32_to_bf16_bits(rng.standard_normal((200, 384)).astype(np.float32))
+    big = np.zeros((200, 512), np.uint16)
+    big[:, :384] = bits
+    x = to_dev_bf16(big)[:, :384]
+    q = torch.full((200, 400), 0xA5, dtype=torch.uint8, device=DEV)
+    s = torch.full((3, 208), -7.0, dtype=torch.float32, device=DEV)
+    pf8._lib.check(pf8.pf8_quant_act_1x128(x.data_ptr(), 200, 384, 512, pf8.PF8_ALONG_COLS, q.data_ptr(), 400,
+                                           s.data_ptr(), 208, torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_act_1x128(bits, "cols")
+    gq, gs = u8(q), f32(s)
+    assert np.array_equal(gq[:, :384], q_ref) and np.all(gq[:, 384:] == 0xA5)
+    assert np.array_equal(gs[:, :200], s_ref) and np.all(gs[:, 200:] == -7.0)
+    # weights with padded pitches, transposed copy too
+    wb = f32_to_bf16_bits((rng.standard_normal((256, 384)) * 0.02).astype(np.float32))
+    wbig = np.zeros((256, 400), np.uint16)
+    wbig[:, :384] = wb
+    w = to_dev_bf16(wbig)
+    qw = torch.full((256, 400), 0x5A, dtype=torch.uint8, device=DEV)
+    qwt = torch.full((384, 272), 0x5A, dtype=torch.uint8, device=DEV)
+    sw = torch.full((2, 5), -1.0, dtype=torch.float32, device=DEV)
+    pf8._lib.check(pf8.pf8_quant_w_128x128(w.data_ptr(), 256, 384, 400, qw.data_ptr(), 400, qwt.data_ptr(), 272,
+                                           sw.data_ptr(), 5, torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    q_ref, qt_ref, s_ref = oracle.quant_w_128x128(wb)
+    assert np.array_equal(u8(qw)[:, :384], q_ref) and np.all(u8(qw)[:, 384:] == 0x5A)
+    assert np.array_equal(u8(qwt)[:, :256], qt_ref) and np.all(u8(qwt)[:, 256:] == 0x5A)
+    assert np.array_equal(f32(sw)[:, :3], s_ref) and np.all(f32(sw)[:, 3:] == -1.0)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    bits = generate("tiny_fprop", only=["X"])["X"]
+    x = to_dev_bf16(bits)
+    a = [pf8.quant_act_1x128(x, "rows") for _ in range(3)]
+    torch.cuda.synchronize()
+    for q, s in a[1:]:
+        assert torch.equal(q, a[0][0]) and torch.equal(s, a[0][1])
