@@ -149,7 +149,7 @@ def time_config_gemms(pf8, torch, reps=20):
     return out
 
 
-def cpu_baseline(sample_tokens=2048):
+def cpu_baseline(sample_tokens=8192):
     """The oracle as it stands, on the first `sample_tokens` tokens of the same layer pass."""
     import oracle
     from workloads import generate
@@ -177,7 +177,7 @@ def cpu_baseline(sample_tokens=2048):
     flops = 3 * 2.0 * m * n * k
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"the same layer pass (all 7 steps, float64 oracle) on the first {m} of 8192 tokens: "
+            "sample": f"the same layer pass (all 7 steps, float64 oracle) on {m} of the 8192 tokens: "
                       f"X [{m},{k}], W [{n},{k}], dY [{m},{n}]; host cpus={os.cpu_count()} "
                       f"affinity={len(os.sched_getaffinity(0))}"}
 

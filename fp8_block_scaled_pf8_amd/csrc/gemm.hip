@@ -25,6 +25,8 @@
 #include "pf8_device.h"
 #include "pf8_launch.h"
 
+#include <type_traits>
+
 namespace pf8 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -317,15 +319,329 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p, int tiles_m, int 
   }
 }
 
+// Scheduling pattern for NM MFMAs: the ND LDS reads go out spread over the first half of the
+// MFMAs (their data is needed at the start of the next stage), the NV vector-memory reads (refill
+// loads, needed only stages later) over the second half (sched_group_barrier masks: 0x008 MFMA,
+// 0x020 VMEM read, 0x100 DS read).
+template <int NM, int NV, int ND, int X = 0>
+__device__ __forceinline__ void interleave_groups() {
+  if constexpr (X < NM) {
+    constexpr int H = NM / 2;
+    constexpr int d = X < H ? (ND * (X + 1)) / H - (ND * X) / H : 0;
+    constexpr int v = X >= H ? (NV * (X - H + 1)) / (NM - H) - (NV * (X - H)) / (NM - H) : 0;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
+    interleave_groups<NM, NV, ND, X + 1>();
+  }
+}
+
+// =============================================================================================
+// MX kernel: direct-to-LDS pipeline.
+//
+//  * K advances in 64-byte stages (one 32x32x64 MFMA k-step; two stages per 128-wide scale block).
+//  * NST stage buffers, each its own LDS object, filled by buffer_load ... lds (16 bytes per lane,
+//    no staging registers) NST-1 stages ahead of use. Each wave issues D = (BM + BN) / 64 such
+//    loads per stage; a wave's load covers 16 rows x 64 bytes.
+//  * 64-byte LDS rows hold 4 chunks of 16 bytes; chunk c of row r sits at c ^ ((r >> 2) & 3). A
+//    b128 operand read serves 16 lanes (16 consecutive rows, one chunk each) per pass over the 64
+//    banks; with this swizzle those 16 chunks land in 16 distinct 4-bank groups.
+//  * Per stage and wave: TM*TN MFMAs split in two halves; between them the wave waits until its own
+//    loads of the next stage have landed and its operand reads are done (explicit s_waitcnt), meets
+//    the others at s_barrier, refills the buffer all waves have just finished reading, and reads the
+//    next stage's operands into the second fragment set while the second half of the MFMAs runs.
+//  * Stage buffer u is used by stages u, u + NST, ...: the loop is unrolled by NST so every buffer
+//    access names a fixed LDS object.
+template <int BM, int BN, bool ROW_B, bool EDGE, int NST>
+__global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+  constexpr int BK = 64;
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int A_ST = BM * BK, ST = (BM + BN) * BK;
+  constexpr int A_DMA = BM / 64, B_DMA = BN / 64, D = A_DMA + B_DMA;  // loads per wave per stage
+  static_assert(NST == 2 || NST == 4, "two or four stage buffers");
+  // four buffers even with NST == 2: the epilogue stages the BM x BN output tile (64 rows per
+  // buffer) through them
+  __shared__ __align__(16) uint8_t buf0[ST];
+  __shared__ __align__(16) uint8_t buf1[ST];
+  __shared__ __align__(16) uint8_t buf2[ST];
+  __shared__ __align__(16) uint8_t buf3[ST];
+  static_assert(64 * BN * 2 <= ST, "64 output rows fit a stage buffer");
+  static_assert(BM <= 256, "at most four 64-row output slabs");
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: keeps LDS and buffer offsets scalar
+  const int wm = wave >> 1, wn = wave & 1;
+
+  int bid = blockIdx.x;
+  {
+    const int nb = gridDim.x, xcd = bid & 7, q = nb >> 3, rem = nb & 7;
+    bid = xcd * q + min(xcd, rem) + (bid >> 3);
+  }
+  constexpr int kGroupM = 8;
+  const int per_group = kGroupM * tiles_n;
+  const int grp = bid / per_group;
+  const int first_m = grp * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int in_grp = bid - grp * per_group;
+  // the divisions above run on the vector ALU; pin the (uniform) tile coordinates to scalars
+  const int tm = __builtin_amdgcn_readfirstlane(first_m + in_grp % gsize);
+  const int tn = __builtin_amdgcn_readfirstlane(in_grp / gsize);
+  const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * BN;
+  const int64_t M = p.m, N = p.n;
+  const int ns = static_cast<int>(p.k / BK);  // stages; a multiple of NST (checked by the launcher)
+
+  // ---- direct-to-LDS loads ----
+  const int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
+  const int rows_a = EDGE ? static_cast<int>(min64(BM, M - m0)) : BM;
+  const int rows_b = EDGE ? static_cast<int>(min64(BN, N - n0)) : BN;
+  const __amdgpu_buffer_rsrc_t rsrc_a =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.a + m0 * p.lda), 0, rows_a * lda, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsrc_b =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.b + n0 * p.ldb), 0, rows_b * ldb, kBufferFlags);
+  // lane -> (row i>>2 of the 16-row slab, LDS chunk i&3); it fetches the chunk that belongs there
+  const int dma_row = lane >> 2;
+  const int dma_chunk = (lane & 3) ^ ((dma_row >> 2) & 3);
+  const int voff_a = dma_row * lda + dma_chunk * 16;
+  const int voff_b = dma_row * ldb + dma_chunk * 16;
+  auto issue_stage = [&](uint8_t* buf, int s) {
+    const int kofs = s * BK;
+#pragma unroll
+    for (int j = 0; j < A_DMA; ++j) {
+      const int slab = wave + 4 * j;  // rows 16*slab .. +15 of the A tile
+      auto* dst = (__attribute__((address_space(3))) void*)(buf + slab * 16 * BK);
+      if (EDGE) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, dst, 16, voff_a + slab * 16 * lda, kofs, 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, dst, 16, voff_a, slab * 16 * lda + kofs, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < B_DMA; ++j) {
+      const int slab = wave + 4 * j;
+      auto* dst = (__attribute__((address_space(3))) void*)(buf + A_ST + slab * 16 * BK);
+      if (EDGE) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, dst, 16, voff_b + slab * 16 * ldb, kofs, 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, dst, 16, voff_b, slab * 16 * ldb + kofs, 0, 0);
+    }
+  };
+
+  // ---- operand fragments ----
+  const int l32 = lane & 31, half = lane >> 5;
+  const int sw = (l32 >> 2) & 3;
+  const int fo0 = l32 * BK + (((2 * half) ^ sw) << 4), fo1 = l32 * BK + (((2 * half + 1) ^ sw) << 4);
+  v8i fa[2][TM], fb[2][TN];
+  auto read_frags = [&](const uint8_t* buf, v8i (&a)[TM], v8i (&b)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int base = (wm * WM + 32 * i) * BK;
+      a[i] = lds_read32(buf, base + fo0, base + fo1);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int base = A_ST + (wn * WN + 32 * j) * BK;
+      b[j] = lds_read32(buf, base + fo0, base + fo1);
+    }
+  };
+
+  // ---- block scales (raw fp32 bits; the E8M0 byte is bits 23..30) ----
+  const int nkb = ns / 2;
+  const int64_t a_row0 = m0 + wm * WM + l32, b_row0 = n0 + wn * WN + l32;
+  uint32_t sa_cur[TM], sb_cur[TN], sa_nxt[TM], sb_nxt[TN];
+  auto load_scales = [&](int kb, uint32_t (&sa)[TM], uint32_t (&sb)[TN]) {
+    kb = min(kb, nkb - 1);  // past the last block: a harmless reload
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      int64_t r = a_row0 + 32 * i;
+      if (EDGE) r = min64(r, M - 1);
+      sa[i] = __float_as_uint(p.a_dscale[static_cast<int64_t>(kb) * p.ld_as + r]);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      int64_t c = b_row0 + 32 * j;
+      if (EDGE) c = min64(c, N - 1);
+      const int64_t idx = ROW_B ? static_cast<int64_t>(kb) * p.sb_k + c * p.sb_n
+                                : (c >> 7) * p.sb_n + static_cast<int64_t>(kb) * p.sb_k;
+      sb[j] = __float_as_uint(p.b_dscale[idx]);
+    }
+  };
+
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto mfma_rows = [&](int f, int i0, int i1) {
+    int sae[TM], sbe[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sae[i] = static_cast<int>(sa_cur[i] >> 23);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sbe[j] = static_cast<int>(sb_cur[j] >> 23);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i < i0 || i >= i1) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0, sbe[j], 0,
+                                                                    sae[i]);
+    }
+  };
+
+  auto bufs = [&](int u) -> uint8_t* { return u == 0 ? buf0 : u == 1 ? buf1 : u == 2 ? buf2 : buf3; };
+  // s_waitcnt: vmcnt(n) with lgkmcnt(0) (and no expcnt wait)
+#define PF8_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0x0 << 8))
+
+  // ---- prologue: stages 0 .. NST-1 in flight, scales of blocks 0 and 1, fragments of stage 0 ----
+  load_scales(0, sa_nxt, sb_nxt);  // before the stage loads, so waiting for it never waits for them
+#pragma unroll
+  for (int u = 0; u < NST; ++u) issue_stage(bufs(u), u);
+  PF8_WAIT_VM_LGKM0(D * (NST - 1));
+  __builtin_amdgcn_s_barrier();
+  read_frags(buf0, fa[0], fb[0]);
+
+  // one stage: s = stage index, u = its buffer (compile-time), refill = issue stage s + NST
+  auto stage = [&](int s, auto u_c, bool refill, auto last_c) {
+    constexpr int u = decltype(u_c)::value;
+    constexpr bool last = decltype(last_c)::value;
+    constexpr int f = u & 1;
+    if constexpr ((u & 1) == 0) {
+      // a new 128-wide scale block starts: rotate, and fetch the next block's scales. The empty
+      // asm hands the value over opaquely, so the compiler cannot start decoding a prefetched
+      // scale (and wait for its load) before this point, two stages after the load was issued.
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        uint32_t v = sa_nxt[i];
+        asm volatile("" : "+v"(v));
+        sa_cur[i] = v;
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        uint32_t v = sb_nxt[j];
+        asm volatile("" : "+v"(v));
+        sb_cur[j] = v;
+      }
+      load_scales(s / 2 + 1, sa_nxt, sb_nxt);
+    }
+    mfma_rows(f, 0, TM / 2);
+    // the first half of the MFMAs stays ahead of the wait and barrier: it keeps the matrix core
+    // busy while the waves line up
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!last) {
+      // stages s+2 .. s+NST-1 may still be in flight (fewer near the end of K)
+      if (refill) PF8_WAIT_VM_LGKM0(D * (NST - 2));
+      else {
+        const int after = ns - 2 - s;  // stages issued after stage s+1
+        if (after >= 2) PF8_WAIT_VM_LGKM0(D * 2);
+        else if (after == 1) PF8_WAIT_VM_LGKM0(D);
+        else PF8_WAIT_VM_LGKM0(0);
+      }
+      __builtin_amdgcn_s_barrier();
+      if (refill) issue_stage(bufs(u), s + NST);
+      read_frags(bufs((u + 1) % NST), fa[f ^ 1], fb[f ^ 1]);
+    }
+    mfma_rows(f, TM / 2, TM);
+    if constexpr (!last) {
+      // spread the refill loads and operand reads over the second half of the MFMAs instead of
+      // issuing them as one burst (which backs up the address FIFO and stalls MFMA issue)
+      interleave_groups<(TM - TM / 2) * TN, D, 2 * (TM + TN)>();
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using F = std::false_type;
+  using T = std::true_type;
+  int s = 0;
+  for (; s < ns - NST; s += NST) {
+    stage(s, I0{}, true, F{});
+    stage(s + 1, I1{}, true, F{});
+    if constexpr (NST == 4) {
+      stage(s + 2, I2{}, true, F{});
+      stage(s + 3, I3{}, true, F{});
+    }
+  }
+  // last NST stages: nothing left to fetch
+  stage(s, I0{}, false, F{});
+  if constexpr (NST == 4) {
+    stage(s + 1, I1{}, false, F{});
+    stage(s + 2, I2{}, false, F{});
+    stage(s + 3, I3{}, false, T{});
+  } else {
+    stage(s + 1, I1{}, false, T{});
+  }
+#undef PF8_WAIT_VM_LGKM0
+
+  // ---- epilogue: BF16 tile staged through LDS, then written as whole rows ----
+  // Lane owns D[m][n .. n+3], m = lane%32 of the MFMA tile, n = 8*(r/4) + 4*(lane/32). Row m of the
+  // tile goes to buffer m/64; its 16-byte chunk c sits at chunk phys(m, c) so that the 32 rows a
+  // wave writes at once spread over the banks, and a wave then reads 16-byte chunks of whole rows
+  // back and stores them contiguously (a 512-byte row per 32 lanes for BN = 256).
+  constexpr int CH = BN / 8;  // 16-byte chunks per output row
+  constexpr int RP = BN * 2;  // output row pitch in LDS (bytes)
+  auto phys = [](int row, int c) -> int {
+    if constexpr ((CH & (CH - 1)) == 0) return c ^ (row & (CH - 1));
+    else return (c + row) % CH;
+  };
+  __builtin_amdgcn_s_barrier();  // every wave is done with the operand buffers
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = wm * WM + 32 * i + l32;
+    uint8_t* rb = bufs(row >> 6) + (row & 63) * RP;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c = (wn * WN + 32 * j + 8 * q4) >> 3;
+        const uint32_t w0 = pack_bf16x2(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1]);
+        const uint32_t w1 = pack_bf16x2(acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]);
+        *reinterpret_cast<uint2*>(rb + phys(row, c) * 16 + 8 * half) = make_uint2(w0, w1);
+      }
+  }
+  __syncthreads();
+  constexpr int PER_T = BM * CH / 256;  // chunks per thread
+#pragma unroll
+  for (int it = 0; it < PER_T; ++it) {
+    const int q = t + 256 * it;
+    const int row = q / CH, c = q % CH;
+    const uint4 v = *reinterpret_cast<const uint4*>(bufs(row >> 6) + (row & 63) * RP + phys(row, c) * 16);
+    const int64_t m = m0 + row, n = n0 + 8 * c;
+    uint16_t* dst = p.d + m * p.ldd + n;
+    if (!EDGE) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else if (m < M) {
+      if (n + 7 < N) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < N) dst[e] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  }
+}
+
 template <int BM, int BN, bool ROW_B, bool MX>
 static hipError_t launch_tile(const GemmArgs& args, hipStream_t stream) {
   const int tiles_m = static_cast<int>((args.m + BM - 1) / BM);
   const int tiles_n = static_cast<int>((args.n + BN - 1) / BN);
   const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n)), block(256);
-  if (args.m % BM == 0 && args.n % BN == 0)
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, ROW_B, MX, false>), grid, block, 0, stream, args, tiles_m, tiles_n);
-  else
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, ROW_B, MX, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
+  const bool edge = args.m % BM != 0 || args.n % BN != 0;
+  if constexpr (MX) {
+    const bool four = (args.k / 64) % 4 == 0;
+    if (edge) {
+      if (four) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 4>), grid, block, 0, stream, args, tiles_m, tiles_n);
+      else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 2>), grid, block, 0, stream, args, tiles_m, tiles_n);
+    } else {
+      if (four) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, false, 4>), grid, block, 0, stream, args, tiles_m, tiles_n);
+      else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, false, 2>), grid, block, 0, stream, args, tiles_m, tiles_n);
+    }
+  } else {
+    if (edge)
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, ROW_B, false, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
+    else
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, ROW_B, false, false>), grid, block, 0, stream, args, tiles_m, tiles_n);
+  }
   return hipGetLastError();
 }
 
