@@ -43,6 +43,11 @@ def parse_args():
     ap.add_argument("--variant", choices=["auto", "mx", "promote"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip timing the per-configuration GEMMs")
+    ap.add_argument("--only", choices=["fprop_gemm", "copy"], default=None,
+                    help="profiling modes: run only the headline fprop GEMM, or only a 1 GiB device copy "
+                         "(the calibration kernel for the FETCH_SIZE / WRITE_SIZE counters), --steps times")
+    ap.add_argument("--summarize-prof", nargs="+", metavar="DIR", default=None,
+                    help="print a text summary of rocprofv3 csv output directories and exit")
     return ap.parse_args()
 
 
@@ -182,8 +187,90 @@ def cpu_baseline(sample_tokens=8192):
                       f"affinity={len(os.sched_getaffinity(0))}"}
 
 
+GEMM_SRC = os.path.join(ROOT, "fp8_block_scaled_pf8_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fprop_gemm_8192x12288x2048_traffic.txt")
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per fprop launch from the committed counter summary, if it matches this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split("=", 1) for line in f.read().splitlines() if "=" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("gemm_source_sha256_16", "").strip() != gemm_source_hash():
+        return None  # the kernel changed since the counters were taken
+    return int(float(kv["hbm_bytes_per_launch"]))
+
+
+def only_mode(args, torch, pf8):
+    """Minimal launch loops for rocprofv3 (no timing output beyond one line)."""
+    from workloads import generate
+
+    if args.only == "copy":
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                          "launches": args.steps}), flush=True)
+        return
+    t = generate(WORKLOAD, only=["X", "W"])
+    qx, sx = pf8.quant_act_1x128(_dev_bf16(t["X"], torch), "cols")
+    qw, _, sw = pf8.quant_w_128x128(_dev_bf16(t["W"], torch), transposed=False)
+    y = torch.empty((qx.shape[0], qw.shape[0]), dtype=torch.bfloat16, device="cuda:0")
+    for _ in range(args.steps):
+        pf8.fprop(qx, sx, qw, sw, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"only": "fprop_gemm", "m": qx.shape[0], "n": qw.shape[0], "k": qx.shape[1],
+                      "launches": args.steps, "gemm_source_sha256_16": gemm_source_hash()}), flush=True)
+
+
+def summarize_prof(dirs):
+    """Text summary of rocprofv3 csv directories: kernel stats and per-dispatch counter averages."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    for d in dirs:
+        print(f"## {d}")
+        for f in sorted(glob.glob(os.path.join(d, "*kernel_stats.csv"))):
+            for r in csv.DictReader(open(f)):
+                print(f"kernel {r['Name'][:90]}: calls={r['Calls']} avg_ns={float(r['AverageNs']):.0f} "
+                      f"min_ns={r['MinNs']} max_ns={r['MaxNs']} pct={float(r['Percentage']):.2f}")
+        for f in sorted(glob.glob(os.path.join(d, "*kernel_trace.csv"))):
+            # per-position view of the layer step: the libpf8 launches repeat in the KERNELS order
+            rows = sorted(csv.DictReader(open(f)), key=lambda r: int(r["Start_Timestamp"]))
+            seq = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows if "pf8::" in r["Kernel_Name"]]
+            nsteps = len(seq) // len(KERNELS)
+            if nsteps >= 3 and len(seq) % len(KERNELS) == 0:
+                skip = 2  # warm-up steps
+                for j, name in enumerate(KERNELS):
+                    v = [seq[i * len(KERNELS) + j] for i in range(skip, nsteps)]
+                    print(f"step position {name}: dispatches={len(v)} avg_ns={sum(v) / len(v):.0f} "
+                          f"min_ns={min(v)} max_ns={max(v)}")
+        for f in sorted(glob.glob(os.path.join(d, "*counter_collection.csv"))):
+            agg = defaultdict(list)
+            for r in csv.DictReader(open(f)):
+                agg[(r["Kernel_Name"][:90], r["Counter_Name"])].append(float(r["Counter_Value"]))
+            for (kname, cname), v in sorted(agg.items()):
+                print(f"counter {cname} kernel {kname}: dispatches={len(v)} avg={sum(v) / len(v):.6g}")
+
+
 def main():
     args = parse_args()
+    if args.summarize_prof:
+        summarize_prof(args.summarize_prof)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); the path has no multi-GPU "
               "mode: each GPU would run this same per-layer pass on its own micro-batch", file=sys.stderr)
@@ -196,6 +283,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(1)
+    if args.only:
+        only_mode(args, torch, pf8)
+        return
     variant = {"auto": pf8.PF8_GEMM_AUTO, "mx": pf8.PF8_GEMM_MX_SCALED, "promote": pf8.PF8_GEMM_PROMOTE}[args.variant]
     wl = WORKLOADS[WORKLOAD]
     t = generate(wl)
@@ -237,8 +327,11 @@ def main():
         kernels[name] = entry
     fp_ms = per["fprop_gemm"]
     achieved = 2.0 * m * n * k / (fp_ms * 1e-3) / 1e12
+    traffic = measured_traffic() if args.variant == "auto" else None
     roofline = {"bound": "mfma", "kernel": "fprop_gemm", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+                "traffic_unit": "bytes per launch (HBM, calibrated FETCH_SIZE + WRITE_SIZE)",
+                "algorithmic_bytes_per_launch": _alg_bytes("fprop_gemm", m, n, k),
                 "algorithmic_flops_per_launch": 2 * m * n * k, "avg_launch_us": round(fp_ms * 1e3, 2)}
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -11,6 +11,11 @@ from __future__ import annotations
 import ctypes
 import os
 
+# libpf8 must run on the same HIP runtime as PyTorch (the streams and device pointers it receives
+# come from PyTorch). Loading PyTorch first makes the dynamic linker resolve libpf8's
+# libamdhip64.so.7 to PyTorch's copy instead of pulling in a second runtime.
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpf8.so")
 
