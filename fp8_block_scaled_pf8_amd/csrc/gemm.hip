@@ -342,29 +342,35 @@ __device__ __forceinline__ void interleave_groups() {
 //  * K advances in 64-byte stages (one 32x32x64 MFMA k-step; two stages per 128-wide scale block).
 //  * NST stage buffers, each its own LDS object, filled by buffer_load ... lds (16 bytes per lane,
 //    no staging registers) NST-1 stages ahead of use. Each wave issues D = (BM + BN) / 64 such
-//    loads per stage; a wave's load covers 16 rows x 64 bytes.
+//    loads per stage; a wave's load covers 16 rows x 64 bytes. With NST = 5 a 256x256 tile uses
+//    all 160 KB of LDS: four stages (128 KB) are in flight while one is consumed.
 //  * 64-byte LDS rows hold 4 chunks of 16 bytes; chunk c of row r sits at c ^ ((r >> 2) & 3). A
 //    b128 operand read serves 16 lanes (16 consecutive rows, one chunk each) per pass over the 64
 //    banks; with this swizzle those 16 chunks land in 16 distinct 4-bank groups.
 //  * Per stage and wave: TM*TN MFMAs split in two halves; between them the wave waits until its own
 //    loads of the next stage have landed and its operand reads are done (explicit s_waitcnt), meets
 //    the others at s_barrier, refills the buffer all waves have just finished reading, and reads the
-//    next stage's operands into the second fragment set while the second half of the MFMAs runs.
-//  * Stage buffer u is used by stages u, u + NST, ...: the loop is unrolled by NST so every buffer
-//    access names a fixed LDS object.
+//    next stage's operands into the other fragment set while the second half of the MFMAs runs.
+//  * Stage s lives in buffer (s - h) mod NST with h = (stage count) mod NST, so that the main loop
+//    (unrolled by NST) and the final NST stages always use buffers 0..NST-1 in order; only the first
+//    h stages (a short head, one code path per h) start elsewhere. Every buffer access thereby names
+//    a fixed LDS object and the compiler can track each buffer's direct-to-LDS loads separately.
+//  * The block scales of a stage travel with its operands: they are loaded into the scale registers
+//    of the stage's buffer when the stage is issued, NST stages before use.
 template <int BM, int BN, bool ROW_B, bool EDGE, int NST>
 __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, int tiles_n) {
   constexpr int BK = 64;
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   constexpr int A_ST = BM * BK, ST = (BM + BN) * BK;
   constexpr int A_DMA = BM / 64, B_DMA = BN / 64, D = A_DMA + B_DMA;  // loads per wave per stage
-  static_assert(NST == 2 || NST == 4, "two or four stage buffers");
-  // four buffers even with NST == 2: the epilogue stages the BM x BN output tile (64 rows per
-  // buffer) through them
+  static_assert(NST == 2 || NST == 4 || NST == 5, "two, four or five stage buffers");
+  // at least four buffers: the epilogue stages the BM x BN output tile (64 rows per buffer) through them
+  constexpr int NBUF = NST < 4 ? 4 : NST;
   __shared__ __align__(16) uint8_t buf0[ST];
   __shared__ __align__(16) uint8_t buf1[ST];
   __shared__ __align__(16) uint8_t buf2[ST];
   __shared__ __align__(16) uint8_t buf3[ST];
+  __shared__ __align__(16) uint8_t buf4[NBUF > 4 ? ST : 16];
   static_assert(64 * BN * 2 <= ST, "64 output rows fit a stage buffer");
   static_assert(BM <= 256, "at most four 64-row output slabs");
 
@@ -388,7 +394,11 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   const int tn = __builtin_amdgcn_readfirstlane(in_grp / gsize);
   const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * BN;
   const int64_t M = p.m, N = p.n;
-  const int ns = static_cast<int>(p.k / BK);  // stages; a multiple of NST (checked by the launcher)
+  const int ns = static_cast<int>(p.k / BK);  // stages (>= NST, checked by the launcher)
+
+  auto bufs = [&](int u) -> uint8_t* {
+    return u == 0 ? buf0 : u == 1 ? buf1 : u == 2 ? buf2 : u == 3 ? buf3 : buf4;
+  };
 
   // ---- direct-to-LDS loads ----
   const int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
@@ -403,7 +413,33 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   const int dma_chunk = (lane & 3) ^ ((dma_row >> 2) & 3);
   const int voff_a = dma_row * lda + dma_chunk * 16;
   const int voff_b = dma_row * ldb + dma_chunk * 16;
-  auto issue_stage = [&](uint8_t* buf, int s) {
+
+  // ---- block scales (raw fp32 bits; the E8M0 byte is bits 23..30), one set per stage buffer ----
+  const int l32 = lane & 31, half = lane >> 5;
+  int64_t a_row[TM], b_row[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a_row[i] = EDGE ? min64(m0 + wm * WM + 32 * i + l32, M - 1) : m0 + wm * WM + 32 * i + l32;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b_row[j] = EDGE ? min64(n0 + wn * WN + 32 * j + l32, N - 1) : n0 + wn * WN + 32 * j + l32;
+  // with tile scales and a wave's columns inside one 128-column tile, one B scale serves all j
+  constexpr bool B_ONE = !ROW_B && (WN == 128) && !EDGE;
+  constexpr int SB = B_ONE ? 1 : TN;
+  uint32_t sc_a[NBUF][TM], sc_b[NBUF][SB];
+  auto load_scales = [&](int s, uint32_t (&sa)[TM], uint32_t (&sb)[SB]) {
+    const int64_t kb = s >> 1;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa[i] = __float_as_uint(p.a_dscale[kb * p.ld_as + a_row[i]]);
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const int64_t idx = ROW_B ? kb * p.sb_k + b_row[j] * p.sb_n : (b_row[j] >> 7) * p.sb_n + kb * p.sb_k;
+      sb[j] = __float_as_uint(p.b_dscale[idx]);
+    }
+  };
+
+  auto issue_stage = [&](auto u_c, int s) {
+    constexpr int u = decltype(u_c)::value;
+    uint8_t* buf = bufs(u);
+    load_scales(s, sc_a[u], sc_b[u]);
     const int kofs = s * BK;
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
@@ -421,44 +457,28 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
     }
   };
 
-  // ---- operand fragments ----
-  const int l32 = lane & 31, half = lane >> 5;
+  // ---- operand fragments: set f = (buffer index) & 1 ----
   const int sw = (l32 >> 2) & 3;
   const int fo0 = l32 * BK + (((2 * half) ^ sw) << 4), fo1 = l32 * BK + (((2 * half + 1) ^ sw) << 4);
   v8i fa[2][TM], fb[2][TN];
-  auto read_frags = [&](const uint8_t* buf, v8i (&a)[TM], v8i (&b)[TN]) {
+  auto read_frags_a = [&](const uint8_t* buf, v8i (&a)[TM], int i0, int i1) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+      if (i < i0 || i >= i1) continue;
       const int base = (wm * WM + 32 * i) * BK;
       a[i] = lds_read32(buf, base + fo0, base + fo1);
     }
+  };
+  auto read_frags_b = [&](const uint8_t* buf, v8i (&b)[TN]) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int base = A_ST + (wn * WN + 32 * j) * BK;
       b[j] = lds_read32(buf, base + fo0, base + fo1);
     }
   };
-
-  // ---- block scales (raw fp32 bits; the E8M0 byte is bits 23..30) ----
-  const int nkb = ns / 2;
-  const int64_t a_row0 = m0 + wm * WM + l32, b_row0 = n0 + wn * WN + l32;
-  uint32_t sa_cur[TM], sb_cur[TN], sa_nxt[TM], sb_nxt[TN];
-  auto load_scales = [&](int kb, uint32_t (&sa)[TM], uint32_t (&sb)[TN]) {
-    kb = min(kb, nkb - 1);  // past the last block: a harmless reload
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      int64_t r = a_row0 + 32 * i;
-      if (EDGE) r = min64(r, M - 1);
-      sa[i] = __float_as_uint(p.a_dscale[static_cast<int64_t>(kb) * p.ld_as + r]);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      int64_t c = b_row0 + 32 * j;
-      if (EDGE) c = min64(c, N - 1);
-      const int64_t idx = ROW_B ? static_cast<int64_t>(kb) * p.sb_k + c * p.sb_n
-                                : (c >> 7) * p.sb_n + static_cast<int64_t>(kb) * p.sb_k;
-      sb[j] = __float_as_uint(p.b_dscale[idx]);
-    }
+  auto read_frags = [&](const uint8_t* buf, v8i (&a)[TM], v8i (&b)[TN]) {
+    read_frags_a(buf, a, 0, TM);
+    read_frags_b(buf, b);
   };
 
   v16f acc[TM][TN];
@@ -469,79 +489,78 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  auto mfma_rows = [&](int f, int i0, int i1) {
-    int sae[TM], sbe[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) sae[i] = static_cast<int>(sa_cur[i] >> 23);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) sbe[j] = static_cast<int>(sb_cur[j] >> 23);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      if (i < i0 || i >= i1) continue;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0, sbe[j], 0,
-                                                                    sae[i]);
-    }
-  };
-
-  auto bufs = [&](int u) -> uint8_t* { return u == 0 ? buf0 : u == 1 ? buf1 : u == 2 ? buf2 : buf3; };
   // s_waitcnt: vmcnt(n) with lgkmcnt(0) (and no expcnt wait)
 #define PF8_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0x0 << 8))
 
-  // ---- prologue: stages 0 .. NST-1 in flight, scales of blocks 0 and 1, fragments of stage 0 ----
-  load_scales(0, sa_nxt, sb_nxt);  // before the stage loads, so waiting for it never waits for them
-#pragma unroll
-  for (int u = 0; u < NST; ++u) issue_stage(bufs(u), u);
-  PF8_WAIT_VM_LGKM0(D * (NST - 1));
-  __builtin_amdgcn_s_barrier();
-  read_frags(buf0, fa[0], fb[0]);
-
-  // one stage: s = stage index, u = its buffer (compile-time), refill = issue stage s + NST
+  // one stage: s = stage index, u = its buffer (compile-time), refill = issue stage s + NST into u
   auto stage = [&](int s, auto u_c, bool refill, auto last_c) {
     constexpr int u = decltype(u_c)::value;
     constexpr bool last = decltype(last_c)::value;
-    constexpr int f = u & 1;
-    if constexpr ((u & 1) == 0) {
-      // a new 128-wide scale block starts: rotate, and fetch the next block's scales. The empty
-      // asm hands the value over opaquely, so the compiler cannot start decoding a prefetched
-      // scale (and wait for its load) before this point, two stages after the load was issued.
+    constexpr int f = u & 1, un = (u + 1) % NST, fn = un & 1;
+    // decode this stage's scales; the empty asm hands each raw value over opaquely so the decode
+    // (and the wait for its load, issued NST stages ago) cannot be hoisted next to the load
+    int sae[TM], sbe[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      uint32_t v = sc_a[u][i];
+      asm volatile("" : "+v"(v));
+      sae[i] = static_cast<int>(v >> 23);
+    }
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      uint32_t v = sc_b[u][j];
+      asm volatile("" : "+v"(v));
+      sbe[j] = static_cast<int>(v >> 23);
+    }
+#pragma unroll
+    for (int j = SB; j < TN; ++j) sbe[j] = sbe[0];
+    auto mfma_rows = [&](int i0, int i1) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        uint32_t v = sa_nxt[i];
-        asm volatile("" : "+v"(v));
-        sa_cur[i] = v;
-      }
+        if (i < i0 || i >= i1) continue;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        uint32_t v = sb_nxt[j];
-        asm volatile("" : "+v"(v));
-        sb_cur[j] = v;
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0, sbe[j],
+                                                                      0, sae[i]);
       }
-      load_scales(s / 2 + 1, sa_nxt, sb_nxt);
-    }
-    mfma_rows(f, 0, TM / 2);
+    };
+    mfma_rows(0, TM / 2);
     // the first half of the MFMAs stays ahead of the wait and barrier: it keeps the matrix core
     // busy while the waves line up
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (!last) {
       // stages s+2 .. s+NST-1 may still be in flight (fewer near the end of K)
-      if (refill) PF8_WAIT_VM_LGKM0(D * (NST - 2));
-      else {
+      if (refill) {
+        PF8_WAIT_VM_LGKM0(D * (NST - 2));
+      } else {
         const int after = ns - 2 - s;  // stages issued after stage s+1
-        if (after >= 2) PF8_WAIT_VM_LGKM0(D * 2);
-        else if (after == 1) PF8_WAIT_VM_LGKM0(D);
-        else PF8_WAIT_VM_LGKM0(0);
+        if constexpr (NST >= 5) {
+          if (after >= 3) PF8_WAIT_VM_LGKM0(D * 3);
+          else if (after == 2) PF8_WAIT_VM_LGKM0(D * 2);
+          else if (after == 1) PF8_WAIT_VM_LGKM0(D);
+          else PF8_WAIT_VM_LGKM0(0);
+        } else {
+          if (after >= 2) PF8_WAIT_VM_LGKM0(D * 2);
+          else if (after == 1) PF8_WAIT_VM_LGKM0(D);
+          else PF8_WAIT_VM_LGKM0(0);
+        }
       }
       __builtin_amdgcn_s_barrier();
-      if (refill) issue_stage(bufs(u), s + NST);
-      read_frags(bufs((u + 1) % NST), fa[f ^ 1], fb[f ^ 1]);
+      if (refill) issue_stage(u_c, s + NST);
+      if constexpr (fn != f) read_frags(bufs(un), fa[fn], fb[fn]);
+      else read_frags_a(bufs(un), fa[fn], 0, TM / 2);  // only A rows the first half no longer needs
     }
-    mfma_rows(f, TM / 2, TM);
+    mfma_rows(TM / 2, TM);
     if constexpr (!last) {
-      // spread the refill loads and operand reads over the second half of the MFMAs instead of
-      // issuing them as one burst (which backs up the address FIFO and stalls MFMA issue)
-      interleave_groups<(TM - TM / 2) * TN, D, 2 * (TM + TN)>();
+      if constexpr (fn != f) {
+        // operand reads early in the second half (needed first thing next stage), refill loads late
+        interleave_groups<(TM - TM / 2) * TN, D + TM + SB, 2 * (TM + TN)>();
+      } else {
+        // with an odd number of buffers the last one hands over to the same fragment set: the
+        // remaining operands are read once the MFMAs above have consumed the registers
+        read_frags_a(bufs(un), fa[fn], TM / 2, TM);
+        read_frags_b(bufs(un), fb[fn]);
+      }
     }
   };
 
@@ -549,24 +568,79 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
   using F = std::false_type;
   using T = std::true_type;
-  int s = 0;
+  auto uc = [](auto x) { return x; };
+  (void)uc;
+
+  // ---- prologue and head: stage s lives in buffer (s - h) mod NST ----
+  const int h = ns % NST;
+  auto prologue = [&](auto h_c) {
+    constexpr int H = decltype(h_c)::value;
+    // stages 0 .. NST-1, issued in stage order (the explicit waits count loads in that order)
+    issue_stage(std::integral_constant<int, (0 - H + NST) % NST>{}, 0);
+    issue_stage(std::integral_constant<int, (1 - H + NST) % NST>{}, 1);
+    if constexpr (NST >= 4) {
+      issue_stage(std::integral_constant<int, (2 - H + NST) % NST>{}, 2);
+      issue_stage(std::integral_constant<int, (3 - H + NST) % NST>{}, 3);
+    }
+    if constexpr (NST >= 5) issue_stage(std::integral_constant<int, (4 - H + NST) % NST>{}, 4);
+    PF8_WAIT_VM_LGKM0(D * (NST - 1));
+    __builtin_amdgcn_s_barrier();
+    constexpr int u0 = (NST - H) % NST;
+    read_frags(bufs(u0), fa[u0 & 1], fb[u0 & 1]);
+    // head stages 0 .. H-1 in buffers NST-H .. NST-1 (all refill: ns >= NST + H)
+    if constexpr (H >= 1) stage(0, std::integral_constant<int, NST - H>{}, true, F{});
+    if constexpr (H >= 2) stage(1, std::integral_constant<int, NST - H + 1>{}, true, F{});
+    if constexpr (H >= 3) stage(2, std::integral_constant<int, NST - H + 2>{}, true, F{});
+    if constexpr (H >= 4) stage(3, std::integral_constant<int, NST - H + 3>{}, true, F{});
+  };
+  if constexpr (NST == 5) {
+    switch (h) {
+      case 0: prologue(I0{}); break;
+      case 1: prologue(I1{}); break;
+      case 2: prologue(I2{}); break;
+      case 3: prologue(I3{}); break;
+      default: prologue(I4{}); break;
+    }
+  } else if constexpr (NST == 4) {
+    switch (h) {
+      case 0: prologue(I0{}); break;
+      case 1: prologue(I1{}); break;
+      case 2: prologue(I2{}); break;
+      default: prologue(I3{}); break;
+    }
+  } else {
+    if (h == 0) prologue(I0{});
+    else prologue(I1{});
+  }
+
+  // ---- main loop: NST stages per trip, buffers 0 .. NST-1 ----
+  int s = h;
   for (; s < ns - NST; s += NST) {
     stage(s, I0{}, true, F{});
     stage(s + 1, I1{}, true, F{});
-    if constexpr (NST == 4) {
+    if constexpr (NST >= 4) {
       stage(s + 2, I2{}, true, F{});
       stage(s + 3, I3{}, true, F{});
     }
+    if constexpr (NST >= 5) stage(s + 4, I4{}, true, F{});
   }
-  // last NST stages: nothing left to fetch
-  stage(s, I0{}, false, F{});
-  if constexpr (NST == 4) {
+  // ---- last NST stages: nothing left to fetch ----
+  if constexpr (NST == 5) {
+    stage(s, I0{}, false, F{});
+    stage(s + 1, I1{}, false, F{});
+    stage(s + 2, I2{}, false, F{});
+    stage(s + 3, I3{}, false, F{});
+    stage(s + 4, I4{}, false, T{});
+  } else if constexpr (NST == 4) {
+    stage(s, I0{}, false, F{});
     stage(s + 1, I1{}, false, F{});
     stage(s + 2, I2{}, false, F{});
     stage(s + 3, I3{}, false, T{});
   } else {
+    stage(s, I0{}, false, F{});
     stage(s + 1, I1{}, false, T{});
   }
 #undef PF8_WAIT_VM_LGKM0
@@ -628,12 +702,17 @@ static hipError_t launch_tile(const GemmArgs& args, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n)), block(256);
   const bool edge = args.m % BM != 0 || args.n % BN != 0;
   if constexpr (MX) {
-    const bool four = (args.k / 64) % 4 == 0;
+    // deepest pipeline that fits the 160 KB LDS and the K extent
+    constexpr int kMaxNst = 5 * (BM + BN) * 64 <= 160 * 1024 ? 5 : 4;
+    const int64_t ns = args.k / 64;
+    const int nst = ns >= kMaxNst ? kMaxNst : (ns >= 4 ? 4 : 2);
     if (edge) {
-      if (four) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 4>), grid, block, 0, stream, args, tiles_m, tiles_n);
+      if (nst == 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, kMaxNst>), grid, block, 0, stream, args, tiles_m, tiles_n);
+      else if (nst == 4) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 4>), grid, block, 0, stream, args, tiles_m, tiles_n);
       else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 2>), grid, block, 0, stream, args, tiles_m, tiles_n);
     } else {
-      if (four) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, false, 4>), grid, block, 0, stream, args, tiles_m, tiles_n);
+      if (nst == 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, false, kMaxNst>), grid, block, 0, stream, args, tiles_m, tiles_n);
+      else if (nst == 4) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, false, 4>), grid, block, 0, stream, args, tiles_m, tiles_n);
       else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, false, 2>), grid, block, 0, stream, args, tiles_m, tiles_n);
     }
   } else {
