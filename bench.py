@@ -2,16 +2,18 @@
 
 A step is one linear layer's full FP8 pass at the fused MLP gate+up shape of a ~2B decoder
 (X [8192, 2048] bf16 = 2 x 4096 tokens, W [12288, 2048], dY [8192, 12288]):
-  quantise X along K, quantise W by 128x128 tiles (+ transposed codes), fprop Y = X W^T,
-  quantise dY along N, dgrad dX = dY W, quantise dY and X along tokens, wgrad dW = dY^T X.
+  quantise X along K and along the tokens (one read), quantise W by 128x128 tiles (+ transposed
+  codes), fprop Y = X W^T, quantise dY along N and along the tokens (one read), dgrad dX = dY W,
+  wgrad dW = dY^T X.  (--unfused: one quantiser pass per orientation, eight launches.)
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 
-Printed (one JSON line): value = the three GEMMs' 2*M*N*K flops per step / step wall time
+Printed (one JSON line): value = the three GEMMs' 2*M*N*K flops per step / step GPU time
 (quantisers included), the fprop GEMM kernel against the FP8 MFMA roofline, per-kernel event
-timings, and the CPU oracle timed on a bounded sample of the same workload.
+timings, hipBLASLt's FP8 / BF16 GEMMs on the fprop shape as context, and the CPU oracle timed on
+a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--variant auto|mx|promote]
-                    [--no-cpu-baseline] [--no-configs]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--variant auto|mx|promote] [--unfused]
+                    [--no-cpu-baseline] [--no-configs] [--no-comparators]
 """
 from __future__ import annotations
 
@@ -31,8 +33,10 @@ METRIC = "FP8 block-scaled GEMM TFLOP/s and % of MI355X FP8 MFMA peak, 1 GPU"
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (AMD published figure, no sparsity)
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "mlp_gateup_layer_step"
-KERNELS = ["quant_x_rows", "quant_w_tiles", "fprop_gemm", "quant_dy_rows", "dgrad_gemm", "quant_dy_cols",
-           "quant_x_cols", "wgrad_gemm"]
+# launch order of one step (LinearStep.launches)
+KERNELS_FUSED = ["quant_x_dual", "quant_w_tiles", "fprop_gemm", "quant_dy_dual", "dgrad_gemm", "wgrad_gemm"]
+KERNELS_UNFUSED = ["quant_x_rows", "quant_w_tiles", "fprop_gemm", "quant_dy_rows", "dgrad_gemm", "quant_dy_cols",
+                   "quant_x_cols", "wgrad_gemm"]
 
 
 def parse_args():
@@ -42,7 +46,9 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--variant", choices=["auto", "mx", "promote"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true", help="one quantiser pass per orientation (eight launches)")
     ap.add_argument("--no-configs", action="store_true", help="skip timing the per-configuration GEMMs")
+    ap.add_argument("--no-comparators", action="store_true", help="skip timing hipBLASLt on the fprop shape")
     ap.add_argument("--only", choices=["fprop_gemm", "copy"], default=None,
                     help="profiling modes: run only the headline fprop GEMM, or only a 1 GiB device copy "
                          "(the calibration kernel for the FETCH_SIZE / WRITE_SIZE counters), --steps times")
@@ -63,6 +69,10 @@ def _alg_bytes(name, m, n, k):
         return rows * cols * 2 + rows * cols + (rows * cols // g) * 4
     if name in ("quant_dy_rows", "quant_dy_cols"):
         return m * n * 2 + m * n + (m * n // g) * 4
+    if name == "quant_x_dual":  # one read, both code sets and scale sets written
+        return m * k * 2 + 2 * (m * k + (m * k // g) * 4)
+    if name == "quant_dy_dual":
+        return m * n * 2 + 2 * (m * n + (m * n // g) * 4)
     if name == "quant_w_tiles":
         return n * k * 2 + 2 * n * k + (n * k // (g * g)) * 4
     if name == "fprop_gemm":
@@ -75,42 +85,56 @@ def _alg_bytes(name, m, n, k):
 
 
 def run_step_timed(step, steps, torch):
-    """Run `steps` steps with an event pair around every kernel launch (all on the current stream)."""
+    """Run `steps` steps with an event after every kernel launch (all on the current stream)."""
     import fp8_block_scaled_pf8_amd._lib as L
 
     st = torch.cuda.current_stream()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(steps)]
-    m, n, k, v = step.m, step.n, step.k, step.variant
-    s = st.cuda_stream
-    c = L.check
-    launches = [
-        lambda: c(L.pf8_quant_act_1x128(step.x.data_ptr(), m, k, k, L.PF8_ALONG_COLS, step.qx.data_ptr(), k,
-                                        step.sx.data_ptr(), m, s)),
-        lambda: c(L.pf8_quant_w_128x128(step.w.data_ptr(), n, k, k, step.qw.data_ptr(), k, step.qwt.data_ptr(), n,
-                                        step.sw.data_ptr(), k // 128, s)),
-        lambda: c(L.pf8_block_gemm_variant(v, L.PF8_FPROP, m, n, k, step.qx.data_ptr(), k, step.sx.data_ptr(), m,
-                                           step.qw.data_ptr(), k, step.sw.data_ptr(), k // 128, 1, step.y.data_ptr(),
-                                           n, s)),
-        lambda: c(L.pf8_quant_act_1x128(step.dy.data_ptr(), m, n, n, L.PF8_ALONG_COLS, step.qdy.data_ptr(), n,
-                                        step.sdy.data_ptr(), m, s)),
-        lambda: c(L.pf8_block_gemm_variant(v, L.PF8_DGRAD, m, k, n, step.qdy.data_ptr(), n, step.sdy.data_ptr(), m,
-                                           step.qwt.data_ptr(), n, step.sw.data_ptr(), 1, k // 128,
-                                           step.dx.data_ptr(), k, s)),
-        lambda: c(L.pf8_quant_act_1x128(step.dy.data_ptr(), m, n, n, L.PF8_ALONG_ROWS, step.qdyt.data_ptr(), m,
-                                        step.sdyt.data_ptr(), n, s)),
-        lambda: c(L.pf8_quant_act_1x128(step.x.data_ptr(), m, k, k, L.PF8_ALONG_ROWS, step.qxt.data_ptr(), m,
-                                        step.sxt.data_ptr(), k, s)),
-        lambda: c(L.pf8_block_gemm_variant(v, L.PF8_WGRAD, n, k, m, step.qdyt.data_ptr(), m, step.sdyt.data_ptr(), n,
-                                           step.qxt.data_ptr(), m, step.sxt.data_ptr(), 1, k, step.dw.data_ptr(), k,
-                                           s)),
-    ]
+    launches = step.launches()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(steps)]
     for i in range(steps):
         e = evs[i]
         e[0].record(st)
-        for j, fn in enumerate(launches):
-            fn()
+        for j, (name, fn) in enumerate(launches):
+            L.check(fn(), name)
             e[j + 1].record(st)
-    return evs
+    return [name for name, _ in launches], evs
+
+
+def time_comparators(torch, m, n, k, reps=20):
+    """hipBLASLt through torch on the fprop shape, as context: FP8 E4M3 with one scale per tensor
+    and per row / column (not block scales), and BF16."""
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = (torch.randn(m, k, device=dev, generator=g) * 0.5).to(torch.float8_e4m3fn)
+    b = (torch.randn(n, k, device=dev, generator=g) * 0.5).to(torch.float8_e4m3fn)
+    one = torch.ones((), device=dev)
+    sa, sb = torch.ones((m, 1), device=dev), torch.ones((1, n), device=dev)
+    ab, bb = a.to(torch.bfloat16), b.to(torch.bfloat16).contiguous()
+    cases = {
+        "hipblaslt_fp8_tensorwise": lambda: torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one,
+                                                             out_dtype=torch.bfloat16),
+        "hipblaslt_fp8_rowwise": lambda: torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16),
+        "hipblaslt_bf16": lambda: torch.mm(ab, bb.t()),
+    }
+    out = {}
+    st = torch.cuda.current_stream()
+    for name, fn in cases.items():
+        try:
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(reps):
+                fn()
+            e1.record(st)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            out[name] = {"us": round(us, 2), "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)}
+        except Exception as ex:  # a comparator that torch cannot run is reported, not fatal
+            out[name] = {"error": repr(ex)[:200]}
+    del a, b, ab, bb
+    torch.cuda.empty_cache()
+    return {"shape": [m, n, k], "note": "library GEMMs without block scales; context only", **out}
 
 
 def time_config_gemms(pf8, torch, reps=20):
@@ -182,7 +206,7 @@ def cpu_baseline(sample_tokens=8192):
     flops = 3 * 2.0 * m * n * k
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"the same layer pass (all 7 steps, float64 oracle) on {m} of the 8192 tokens: "
+            "sample": f"the same layer pass (quantisers and the three GEMMs, float64 oracle) on {m} of the 8192 tokens: "
                       f"X [{m},{k}], W [{n},{k}], dY [{m},{n}]; host cpus={os.cpu_count()} "
                       f"affinity={len(os.sched_getaffinity(0))}"}
 
@@ -248,14 +272,17 @@ def summarize_prof(dirs):
                 print(f"kernel {r['Name'][:90]}: calls={r['Calls']} avg_ns={float(r['AverageNs']):.0f} "
                       f"min_ns={r['MinNs']} max_ns={r['MaxNs']} pct={float(r['Percentage']):.2f}")
         for f in sorted(glob.glob(os.path.join(d, "*kernel_trace.csv"))):
-            # per-position view of the layer step: the libpf8 launches repeat in the KERNELS order
+            # per-position view of the layer step: the libpf8 launches repeat in LinearStep order
             rows = sorted(csv.DictReader(open(f)), key=lambda r: int(r["Start_Timestamp"]))
-            seq = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows if "pf8::" in r["Kernel_Name"]]
-            nsteps = len(seq) // len(KERNELS)
-            if nsteps >= 3 and len(seq) % len(KERNELS) == 0:
+            pf8_rows = [r for r in rows if "pf8::" in r["Kernel_Name"]]
+            seq = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in pf8_rows]
+            dual = any("quant_dual" in r["Kernel_Name"] for r in pf8_rows)
+            kernels = KERNELS_FUSED if dual else KERNELS_UNFUSED
+            nsteps = len(seq) // len(kernels)
+            if nsteps >= 3 and len(seq) % len(kernels) == 0:
                 skip = 2  # warm-up steps
-                for j, name in enumerate(KERNELS):
-                    v = [seq[i * len(KERNELS) + j] for i in range(skip, nsteps)]
+                for j, name in enumerate(kernels):
+                    v = [seq[i * len(kernels) + j] for i in range(skip, nsteps)]
                     print(f"step position {name}: dispatches={len(v)} avg_ns={sum(v) / len(v):.0f} "
                           f"min_ns={min(v)} max_ns={max(v)}")
         for f in sorted(glob.glob(os.path.join(d, "*counter_collection.csv"))):
@@ -291,23 +318,24 @@ def main():
     t = generate(wl)
     x, w, dy = (_dev_bf16(t[nm], torch) for nm in ("X", "W", "dY"))
     del t
-    step = pf8.LinearStep(x, w, dy, variant=variant)
+    step = pf8.LinearStep(x, w, dy, variant=variant, fused=not args.unfused)
     m, n, k = step.m, step.n, step.k
-    print(f"# workload {WORKLOAD}: M={m} N={n} K={k}, variant={args.variant}", file=sys.stderr, flush=True)
+    print(f"# workload {WORKLOAD}: M={m} N={n} K={k}, variant={args.variant}, "
+          f"{'unfused' if args.unfused else 'dual-orientation'} quantisers", file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    evs = run_step_timed(step, args.steps, torch)
+    names, evs = run_step_timed(step, args.steps, torch)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step_wall = wall * 1e3 / args.steps
     # per-kernel averages from the events (same stream as the launches)
-    per = {name: 0.0 for name in KERNELS}
+    per = {name: 0.0 for name in names}
     gpu_ms = 0.0
     for e in evs:
-        for j, name in enumerate(KERNELS):
+        for j, name in enumerate(names):
             per[name] += e[j].elapsed_time(e[j + 1])
         gpu_ms += e[0].elapsed_time(e[-1])
     per = {kname: v / args.steps for kname, v in per.items()}
@@ -315,7 +343,7 @@ def main():
     flops = step.flops()
     value = flops / (ms_step * 1e-3) / 1e12
     kernels = {}
-    for name in KERNELS:
+    for name in names:
         ms = per[name]
         entry = {"us": round(ms * 1e3, 2)}
         if name.endswith("gemm"):
@@ -338,16 +366,19 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
         "config": {"workload": WORKLOAD, "m_tokens": m, "n": n, "k": k, "gemms": ["fprop", "dgrad", "wgrad"],
-                   "variant": args.variant, "title": wl.title},
+                   "variant": args.variant, "quantisers": "single" if args.unfused else "dual",
+                   "launches_per_step": len(names), "title": wl.title},
         "pct_of_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
         "wall_ms_per_step": round(ms_step_wall, 4),
         "roofline": roofline,
         "kernels": kernels,
     }
+    del step, x, w, dy
+    torch.cuda.empty_cache()
     if not args.no_configs:
-        del step, x, w, dy
-        torch.cuda.empty_cache()
         result["config_gemms"] = time_config_gemms(pf8, torch)
+    if not args.no_comparators:
+        result["comparators"] = time_comparators(torch, m, n, k)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)

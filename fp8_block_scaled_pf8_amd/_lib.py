@@ -23,7 +23,7 @@ PF8_OK, PF8_EINVAL, PF8_ESHAPE, PF8_EALIGN, PF8_ENODEV, PF8_ELAUNCH = range(6)
 PF8_ALONG_COLS, PF8_ALONG_ROWS = 0, 1
 PF8_FPROP, PF8_DGRAD, PF8_WGRAD = 0, 1, 2
 PF8_GEMM_AUTO, PF8_GEMM_MX_SCALED, PF8_GEMM_PROMOTE = 0, 1, 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
@@ -32,6 +32,7 @@ _vp = ctypes.c_void_p
 # name -> (restype, argtypes); mirrors include/pf8.h
 SIGNATURES = {
     "pf8_quant_act_1x128": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp]),
+    "pf8_quant_act_dual": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
     "pf8_quant_w_128x128": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
     "pf8_block_gemm": (_int, [_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
     "pf8_block_gemm_variant": (
@@ -44,7 +45,7 @@ SIGNATURES = {
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"libpf8.so is not built ({LIB_PATH}); run `python -m fp8_block_scaled_pf8_amd.build` "
+            f"libpf8.so is not built ({LIB_PATH}); run `python fp8_block_scaled_pf8_amd/build.py` "
             "(or __graft_entry__.build()) first")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
@@ -61,6 +62,12 @@ LIB = _load()
 
 def pf8_quant_act_1x128(x, rows, cols, ldx, axis, q, ldq, dscale, ld_s, hip_stream=0) -> int:
     return LIB.pf8_quant_act_1x128(x, rows, cols, ldx, axis, q, ldq, dscale, ld_s, hip_stream)
+
+
+def pf8_quant_act_dual(x, rows, cols, ldx, q_row, ldq_row, dscale_row, ld_sr, q_col, ldq_col, dscale_col, ld_sc,
+                       hip_stream=0) -> int:
+    return LIB.pf8_quant_act_dual(x, rows, cols, ldx, q_row, ldq_row, dscale_row, ld_sr, q_col, ldq_col, dscale_col,
+                                  ld_sc, hip_stream)
 
 
 def pf8_quant_w_128x128(w, n, k, ldw, q, ldq, qt, ldqt, dscale, ld_s, hip_stream=0) -> int:

@@ -1,6 +1,8 @@
 """Build libpf8.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-    python -m fp8_block_scaled_pf8_amd.build [--asm DIR]
+    python fp8_block_scaled_pf8_amd/build.py [--asm DIR]
+
+(run as a file: importing the package first would load the library being rebuilt)
 
 --asm DIR additionally writes the gfx950 assembly of every source into DIR.
 """

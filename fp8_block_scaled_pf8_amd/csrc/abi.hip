@@ -67,6 +67,23 @@ int pf8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx, 
   return launch_status(e);
 }
 
+int pf8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q_row, int64_t ldq_row,
+                       float* dscale_row, int64_t ld_sr, void* q_col, int64_t ldq_col, float* dscale_col, int64_t ld_sc,
+                       void* hip_stream) {
+  if (x == nullptr || q_row == nullptr || dscale_row == nullptr || q_col == nullptr || dscale_col == nullptr)
+    return PF8_EINVAL;
+  if (rows <= 0 || cols <= 0) return PF8_EINVAL;
+  if (rows % kGroup != 0 || cols % kGroup != 0) return PF8_ESHAPE;
+  if (ldx < cols || ldq_row < cols || ld_sr < rows || ldq_col < rows || ld_sc < cols) return PF8_EINVAL;
+  if (!aligned16(x) || !aligned16(q_row) || !aligned16(q_col) || !aligned4(dscale_row) || !aligned4(dscale_col))
+    return PF8_EALIGN;
+  if ((ldx * 2) % 16 != 0 || ldq_row % 16 != 0 || ldq_col % 16 != 0) return PF8_EALIGN;
+  if (rows / kGroup > 65535 || cols / kGroup > (int64_t{1} << 31) - 1) return PF8_ESHAPE;  // grid (cols/128, rows/128)
+  if (int s = device_status(); s != PF8_OK) return s;
+  return launch_status(pf8::launch_quant_dual(x, rows, cols, ldx, q_row, ldq_row, dscale_row, ld_sr, q_col, ldq_col,
+                                              dscale_col, ld_sc, static_cast<hipStream_t>(hip_stream)));
+}
+
 int pf8_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw, void* q, int64_t ldq, void* qt, int64_t ldqt,
                         float* dscale, int64_t ld_s, void* hip_stream) {
   if (w == nullptr || q == nullptr || dscale == nullptr) return PF8_EINVAL;

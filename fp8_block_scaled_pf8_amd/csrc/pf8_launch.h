@@ -10,6 +10,9 @@ hipError_t launch_quant_rows(const void* x, int64_t rows, int64_t cols, int64_t 
                              float* dscale, int64_t ld_s, hipStream_t stream);
 hipError_t launch_quant_cols(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q, int64_t ldq,
                              float* dscale, int64_t ld_s, hipStream_t stream);
+hipError_t launch_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q_row, int64_t ldq_row,
+                             float* dscale_row, int64_t ld_sr, void* q_col, int64_t ldq_col, float* dscale_col,
+                             int64_t ld_sc, hipStream_t stream);
 hipError_t launch_quant_w(const void* w, int64_t n, int64_t k, int64_t ldw, void* q, int64_t ldq, void* qt,
                           int64_t ldqt, float* dscale, int64_t ld_s, hipStream_t stream);
 

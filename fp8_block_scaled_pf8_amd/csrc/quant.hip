@@ -207,6 +207,120 @@ __global__ __launch_bounds__(256) void quant_w_kernel(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------------------------------------
+// Both orientations from one read: a workgroup takes a 128 x 128 tile, which is 128 row groups
+// (one per row, along the columns) and 128 column groups (one per column, along the rows).
+//   thread t holds rows 8*(t/16) .. +7, columns 8*(t%16) .. +7 (eight 16-byte loads);
+//   row mode: a row's maximum is reduced over its 16 lanes (one DPP row), codes go straight out;
+//   col mode: per-column maxima over the thread's 8 rows (packed 16-bit max), then over the wave
+//   (xor 16, 32) and the 4 waves in LDS; for column j the thread's 8 codes (rows 8*(t/16) ..)
+//   form one 64-bit word, written to an LDS tile [128 cols][128 rows] and sent out as 128-byte
+//   rows of the transposed code matrix.
+// LDS tile: rows c, c+1 (c even) share 256 bytes = all 64 banks; 8-byte slot s of row c sits at
+// slot (s | (c & 1) << 4) ^ (((c >> 3) & 7) << 2) of the pair, so a 16-lane read of two rows'
+// 16-byte chunks touches every bank once.
+typedef unsigned short ushort2_v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  const ushort2_v r = __builtin_elementwise_max(__builtin_bit_cast(ushort2_v, a), __builtin_bit_cast(ushort2_v, b));
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ int dual_slot(int c, int s) {
+  return (c >> 1) * 256 + 8 * ((s | ((c & 1) << 4)) ^ (((c >> 3) & 7) << 2));
+}
+
+__global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                         uint8_t* __restrict__ qr, int64_t ldqr,
+                                                         float* __restrict__ sr, int64_t ld_sr,
+                                                         uint8_t* __restrict__ qc, int64_t ldqc,
+                                                         float* __restrict__ sc, int64_t ld_sc) {
+  __shared__ __align__(16) uint32_t red[4][16][4];  // [wave][column chunk][packed column pair]
+  __shared__ __align__(16) uint8_t tile[kGroup * kGroup];
+  const int t = threadIdx.x;
+  const int rb = t >> 4;  // rows 8*rb .. 8*rb+7 of the tile
+  const int cc = t & 15;  // cols 8*cc .. 8*cc+7 of the tile
+  const int wave = t >> 6;
+  const int64_t gc = blockIdx.x, gr = blockIdx.y;  // column group (row mode), row group (col mode)
+  const int64_t r0 = gr * kGroup, c0 = gc * kGroup;
+  uint4 v[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) v[p] = *reinterpret_cast<const uint4*>(x + (r0 + 8 * rb + p) * ldx + c0 + 8 * cc);
+
+  // ---- row mode: 8 rows, one 128-value group each ----
+  float my_row_scale = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int e = block_exponent(row16_max(amax8_bits(v[p])));
+    *reinterpret_cast<uint2*>(qr + (r0 + 8 * rb + p) * ldqr + c0 + 8 * cc) = quant8(v[p], pow2f(-e));
+    if (cc == p) my_row_scale = pow2f(e);
+  }
+  if (cc < 8) sr[gc * ld_sr + r0 + 8 * rb + cc] = my_row_scale;
+
+  // ---- col mode: per-column maxima, packed as column pairs (2h, 2h+1) in word h ----
+  uint32_t m[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) m[h] = 0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint32_t w[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) m[h] = pk_max_u16(m[h], w[h] & 0x7FFF7FFFu);
+  }
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    m[h] = pk_max_u16(m[h], static_cast<uint32_t>(__shfl_xor(static_cast<int>(m[h]), 16)));
+    m[h] = pk_max_u16(m[h], static_cast<uint32_t>(__shfl_xor(static_cast<int>(m[h]), 32)));
+  }
+  if ((t & 63) < 16) *reinterpret_cast<uint4*>(&red[wave][cc][0]) = make_uint4(m[0], m[1], m[2], m[3]);
+  __syncthreads();
+  float inv[8];
+  {
+    uint4 a = *reinterpret_cast<const uint4*>(&red[0][cc][0]);
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const uint4 b = *reinterpret_cast<const uint4*>(&red[w][cc][0]);
+      a = make_uint4(pk_max_u16(a.x, b.x), pk_max_u16(a.y, b.y), pk_max_u16(a.z, b.z), pk_max_u16(a.w, b.w));
+    }
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+    float my_col_scale = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = block_exponent((aw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+      inv[j] = pow2f(-e);
+      if (rb == j) my_col_scale = pow2f(e);
+    }
+    // thread (rb < 8, cc) writes the scale of column 8*cc + rb
+    if (rb < 8) sc[gr * ld_sc + c0 + 8 * cc + rb] = my_col_scale;
+  }
+  // codes of column j for rows 8*rb .. 8*rb+7: one little-endian 64-bit word
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int h = j >> 1;
+    float f[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const uint32_t w = h == 0 ? v[p].x : h == 1 ? v[p].y : h == 2 ? v[p].z : v[p].w;
+      f[p] = ((j & 1) ? bf16_hi(w) : bf16_lo(w)) * inv[j];
+    }
+    int lo = cvt2_e4m3<false>(f[0], f[1], 0);
+    lo = cvt2_e4m3<true>(f[2], f[3], lo);
+    int hi = cvt2_e4m3<false>(f[4], f[5], 0);
+    hi = cvt2_e4m3<true>(f[6], f[7], hi);
+    *reinterpret_cast<uint2*>(tile + dual_slot(8 * cc + j, rb)) =
+        make_uint2(static_cast<uint32_t>(lo), static_cast<uint32_t>(hi));
+  }
+  __syncthreads();
+  // 128 transposed rows of 128 bytes: thread t sends chunk (t & 7) of rows (t >> 3) + 32 * i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = (t >> 3) + 32 * i;
+    const int k = t & 7;
+    const uint4 val = *reinterpret_cast<const uint4*>(tile + dual_slot(c, 2 * k));
+    *reinterpret_cast<uint4*>(qc + (c0 + c) * ldqc + r0 + 16 * k) = val;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 hipError_t launch_quant_rows(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q, int64_t ldq,
                              float* dscale, int64_t ld_s, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((rows + kRowsPerWG - 1) / kRowsPerWG), static_cast<unsigned>(cols / kGroup));
@@ -228,6 +342,16 @@ hipError_t launch_quant_w(const void* w, int64_t n, int64_t k, int64_t ldw, void
   const dim3 grid(static_cast<unsigned>(k / kGroup), static_cast<unsigned>(n / kGroup));
   hipLaunchKernelGGL(quant_w_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(w), ldw,
                      static_cast<uint8_t*>(q), ldq, static_cast<uint8_t*>(qt), ldqt, dscale, ld_s);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q_row, int64_t ldq_row,
+                             float* dscale_row, int64_t ld_sr, void* q_col, int64_t ldq_col, float* dscale_col,
+                             int64_t ld_sc, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(cols / kGroup), static_cast<unsigned>(rows / kGroup));
+  hipLaunchKernelGGL(quant_dual_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(x), ldx,
+                     static_cast<uint8_t*>(q_row), ldq_row, dscale_row, ld_sr, static_cast<uint8_t*>(q_col), ldq_col,
+                     dscale_col, ld_sc);
   return hipGetLastError();
 }
 

@@ -58,6 +58,23 @@ def quant_act_1x128(x: torch.Tensor, along: str = "cols") -> Tuple[torch.Tensor,
     return q, s
 
 
+def quant_act_dual(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Both 1x128 groupings from one read of x [R, C] (R, C multiples of 128).
+
+    Returns (q_row [R, C], s_row [C/128, R], q_col [C, R], s_col [R/128, C]), bit-identical to
+    quant_act_1x128(x, "cols") and quant_act_1x128(x, "rows").
+    """
+    _check_2d(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    e = lambda *sh, dt=torch.uint8: torch.empty(sh, dtype=dt, device=x.device)  # noqa: E731
+    qr, sr = e(rows, cols), e(max(cols // GROUP, 1), rows, dt=torch.float32)
+    qc, sc = e(cols, rows), e(max(rows // GROUP, 1), cols, dt=torch.float32)
+    L.check(L.pf8_quant_act_dual(x.data_ptr(), rows, cols, x.stride(0), qr.data_ptr(), qr.stride(0), sr.data_ptr(),
+                                 sr.stride(0), qc.data_ptr(), qc.stride(0), sc.data_ptr(), sc.stride(0), _stream(x)),
+            "pf8_quant_act_dual")
+    return qr, sr, qc, sc
+
+
 def quant_w_128x128(w: torch.Tensor, transposed: bool = True
                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor], torch.Tensor]:
     """128x128-tile power-of-two E4M3 quantisation of a weight; optionally also the transposed codes."""
@@ -116,18 +133,24 @@ def wgrad(qdyt, sdy, qxt, sx, out=None, variant: int = L.PF8_GEMM_AUTO) -> torch
 class LinearStep:
     """One linear layer's FP8 training pass at a fixed shape, with every buffer preallocated.
 
-    forward:  X [M, K] -> codes along K, W [N, K] -> tile codes (+ transposed), Y = X . W^T
-    backward: dY [M, N] -> codes along N, dX = dY . W; dY and X -> codes along M, dW = dY^T . X
-    ``run`` enqueues the seven kernels on the current stream and allocates nothing.
+    forward:  X [M, K] -> codes along K (and along M for the weight gradient),
+              W [N, K] -> tile codes (+ transposed), Y = X . W^T
+    backward: dY [M, N] -> codes along N and along M, dX = dY . W, dW = dY^T . X
+    With ``fused`` (the default; needs M, N, K multiples of 128) X and dY are each read once by
+    the dual-orientation quantiser: six launches. Otherwise each orientation has its own pass:
+    eight launches. ``run`` enqueues them on the current stream and allocates nothing.
     """
 
-    def __init__(self, x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, variant: int = L.PF8_GEMM_AUTO):
+    def __init__(self, x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, variant: int = L.PF8_GEMM_AUTO,
+                 fused: bool = True):
         for t, name in ((x, "x"), (w, "w"), (dy, "dy")):
             _check_2d(t, torch.bfloat16, name)
         (m, k), (n, k2), (m2, n2) = x.shape, w.shape, dy.shape
         if k != k2 or m != m2 or n != n2:
             raise ValueError("inconsistent shapes for X [M,K], W [N,K], dY [M,N]")
-        self.x, self.w, self.dy, self.variant = x, w, dy, variant
+        if fused and (m % GROUP or n % GROUP or k % GROUP):
+            raise ValueError("the fused step needs M, N and K to be multiples of 128")
+        self.x, self.w, self.dy, self.variant, self.fused = x, w, dy, variant, fused
         self.m, self.n, self.k = m, n, k
         dev = x.device
         u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
@@ -142,26 +165,41 @@ class LinearStep:
     def flops(self) -> int:
         return 3 * 2 * self.m * self.n * self.k
 
-    def run(self) -> None:
+    def launches(self):
+        """The step as a list of (name, thunk); each thunk enqueues one kernel and returns its status."""
         st = torch.cuda.current_stream(self.x.device).cuda_stream
         m, n, k, v = self.m, self.n, self.k, self.variant
-        c = L.check
-        c(L.pf8_quant_act_1x128(self.x.data_ptr(), m, k, self.x.stride(0), L.PF8_ALONG_COLS, self.qx.data_ptr(), k,
-                                self.sx.data_ptr(), m, st), "quant X")
-        c(L.pf8_quant_w_128x128(self.w.data_ptr(), n, k, self.w.stride(0), self.qw.data_ptr(), k, self.qwt.data_ptr(),
-                                n, self.sw.data_ptr(), k // GROUP, st), "quant W")
-        c(L.pf8_block_gemm_variant(v, L.PF8_FPROP, m, n, k, self.qx.data_ptr(), k, self.sx.data_ptr(), m,
-                                   self.qw.data_ptr(), k, self.sw.data_ptr(), k // GROUP, 1, self.y.data_ptr(), n, st),
-          "fprop")
-        c(L.pf8_quant_act_1x128(self.dy.data_ptr(), m, n, self.dy.stride(0), L.PF8_ALONG_COLS, self.qdy.data_ptr(), n,
-                                self.sdy.data_ptr(), m, st), "quant dY")
-        c(L.pf8_block_gemm_variant(v, L.PF8_DGRAD, m, k, n, self.qdy.data_ptr(), n, self.sdy.data_ptr(), m,
-                                   self.qwt.data_ptr(), n, self.sw.data_ptr(), 1, k // GROUP, self.dx.data_ptr(), k,
-                                   st), "dgrad")
-        c(L.pf8_quant_act_1x128(self.dy.data_ptr(), m, n, self.dy.stride(0), L.PF8_ALONG_ROWS, self.qdyt.data_ptr(), m,
-                                self.sdyt.data_ptr(), n, st), "quant dY^T")
-        c(L.pf8_quant_act_1x128(self.x.data_ptr(), m, k, self.x.stride(0), L.PF8_ALONG_ROWS, self.qxt.data_ptr(), m,
-                                self.sxt.data_ptr(), k, st), "quant X^T")
-        c(L.pf8_block_gemm_variant(v, L.PF8_WGRAD, n, k, m, self.qdyt.data_ptr(), m, self.sdyt.data_ptr(), n,
-                                   self.qxt.data_ptr(), m, self.sxt.data_ptr(), 1, k, self.dw.data_ptr(), k, st),
-          "wgrad")
+        x, dy = self.x, self.dy
+        quant_x_rows = ("quant_x_rows", lambda: L.pf8_quant_act_1x128(
+            x.data_ptr(), m, k, x.stride(0), L.PF8_ALONG_COLS, self.qx.data_ptr(), k, self.sx.data_ptr(), m, st))
+        quant_x_cols = ("quant_x_cols", lambda: L.pf8_quant_act_1x128(
+            x.data_ptr(), m, k, x.stride(0), L.PF8_ALONG_ROWS, self.qxt.data_ptr(), m, self.sxt.data_ptr(), k, st))
+        quant_x_dual = ("quant_x_dual", lambda: L.pf8_quant_act_dual(
+            x.data_ptr(), m, k, x.stride(0), self.qx.data_ptr(), k, self.sx.data_ptr(), m, self.qxt.data_ptr(), m,
+            self.sxt.data_ptr(), k, st))
+        quant_w = ("quant_w_tiles", lambda: L.pf8_quant_w_128x128(
+            self.w.data_ptr(), n, k, self.w.stride(0), self.qw.data_ptr(), k, self.qwt.data_ptr(), n,
+            self.sw.data_ptr(), k // GROUP, st))
+        fprop = ("fprop_gemm", lambda: L.pf8_block_gemm_variant(
+            v, L.PF8_FPROP, m, n, k, self.qx.data_ptr(), k, self.sx.data_ptr(), m, self.qw.data_ptr(), k,
+            self.sw.data_ptr(), k // GROUP, 1, self.y.data_ptr(), n, st))
+        quant_dy_rows = ("quant_dy_rows", lambda: L.pf8_quant_act_1x128(
+            dy.data_ptr(), m, n, dy.stride(0), L.PF8_ALONG_COLS, self.qdy.data_ptr(), n, self.sdy.data_ptr(), m, st))
+        quant_dy_cols = ("quant_dy_cols", lambda: L.pf8_quant_act_1x128(
+            dy.data_ptr(), m, n, dy.stride(0), L.PF8_ALONG_ROWS, self.qdyt.data_ptr(), m, self.sdyt.data_ptr(), n, st))
+        quant_dy_dual = ("quant_dy_dual", lambda: L.pf8_quant_act_dual(
+            dy.data_ptr(), m, n, dy.stride(0), self.qdy.data_ptr(), n, self.sdy.data_ptr(), m, self.qdyt.data_ptr(), m,
+            self.sdyt.data_ptr(), n, st))
+        dgrad = ("dgrad_gemm", lambda: L.pf8_block_gemm_variant(
+            v, L.PF8_DGRAD, m, k, n, self.qdy.data_ptr(), n, self.sdy.data_ptr(), m, self.qwt.data_ptr(), n,
+            self.sw.data_ptr(), 1, k // GROUP, self.dx.data_ptr(), k, st))
+        wgrad = ("wgrad_gemm", lambda: L.pf8_block_gemm_variant(
+            v, L.PF8_WGRAD, n, k, m, self.qdyt.data_ptr(), m, self.sdyt.data_ptr(), n, self.qxt.data_ptr(), m,
+            self.sxt.data_ptr(), 1, k, self.dw.data_ptr(), k, st))
+        if self.fused:
+            return [quant_x_dual, quant_w, fprop, quant_dy_dual, dgrad, wgrad]
+        return [quant_x_rows, quant_w, fprop, quant_dy_rows, dgrad, quant_dy_cols, quant_x_cols, wgrad]
+
+    def run(self) -> None:
+        for name, launch in self.launches():
+            L.check(launch(), name)

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define PF8_ABI_VERSION 1
+#define PF8_ABI_VERSION 2
 
 /* Status codes (int). */
 #define PF8_OK 0
@@ -76,6 +76,23 @@ extern "C" {
  */
 int pf8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
                         void* q, int64_t ldq, float* dscale, int64_t ld_s, void* hip_stream);
+
+/*
+ * Dual-orientation 1x128 quantiser [same passages as above; the forward pass needs X grouped
+ * along K for Y = X.W^T and along the tokens for dW = dY^T.X, the backward pass dY along N for
+ * dX = dY.W and along the tokens for dW]: one read of x yields both groupings.
+ *
+ * x: bf16 [rows, cols], row pitch ldx >= cols; requires rows % 128 == 0 and cols % 128 == 0.
+ * Row mode (groups of 128 along a row), exactly as pf8_quant_act_1x128 with PF8_ALONG_COLS:
+ *     q_row: u8 [rows, cols], pitch ldq_row >= cols; dscale_row[g * ld_sr + r], ld_sr >= rows.
+ * Col mode (groups of 128 along a column), exactly as pf8_quant_act_1x128 with PF8_ALONG_ROWS:
+ *     q_col: u8 [cols, rows] (transposed), pitch ldq_col >= rows; dscale_col[g * ld_sc + c], ld_sc >= cols.
+ * The four outputs are bit-identical to those of the two single-orientation calls.
+ * Returns PF8_OK, PF8_EINVAL, PF8_ESHAPE, PF8_EALIGN, PF8_ENODEV or PF8_ELAUNCH.
+ */
+int pf8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                       void* q_row, int64_t ldq_row, float* dscale_row, int64_t ld_sr,
+                       void* q_col, int64_t ldq_col, float* dscale_col, int64_t ld_sc, void* hip_stream);
 
 /*
  * 128x128 weight-tile quantiser [paper.rainbus.top summary, section "FP8 块级混合精度训练" and

@@ -25,8 +25,8 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert names == sorted(["pf8_quant_act_1x128", "pf8_quant_w_128x128", "pf8_block_gemm", "pf8_block_gemm_variant",
-                            "pf8_strerror", "pf8_abi_version"])
+    assert names == sorted(["pf8_quant_act_1x128", "pf8_quant_act_dual", "pf8_quant_w_128x128", "pf8_block_gemm",
+                            "pf8_block_gemm_variant", "pf8_strerror", "pf8_abi_version"])
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -78,6 +78,34 @@ def test_quant_act_validation():
     assert _qa(axis=L.PF8_ALONG_ROWS, cols=508, ldx=512, ldq=256, ld_s=508) == L.PF8_ESHAPE
     assert _qa(axis=L.PF8_ALONG_ROWS, ldq=128, ld_s=512) == L.PF8_EINVAL
     assert _qa(axis=L.PF8_ALONG_ROWS, ldq=256, ld_s=500) == L.PF8_EINVAL
+
+
+def _qd(**kw):
+    a = dict(x=A16, rows=256, cols=384, ldx=384, qr=B16, ldqr=384, sr=S4, ld_sr=256, qc=C16, ldqc=256, sc=S4,
+             ld_sc=384)
+    a.update(kw)
+    return L.pf8_quant_act_dual(a["x"], a["rows"], a["cols"], a["ldx"], a["qr"], a["ldqr"], a["sr"], a["ld_sr"],
+                                a["qc"], a["ldqc"], a["sc"], a["ld_sc"], 0)
+
+
+def test_quant_dual_validation():
+    for key in ["x", "qr", "sr", "qc", "sc"]:
+        assert _qd(**{key: 0}) == L.PF8_EINVAL, key
+    assert _qd(rows=0) == L.PF8_EINVAL
+    assert _qd(cols=-128) == L.PF8_EINVAL
+    assert _qd(rows=200) == L.PF8_ESHAPE  # both dimensions are grouped
+    assert _qd(cols=200, ldx=384) == L.PF8_ESHAPE
+    assert _qd(ldx=256) == L.PF8_EINVAL
+    assert _qd(ldqr=256) == L.PF8_EINVAL
+    assert _qd(ld_sr=128) == L.PF8_EINVAL
+    assert _qd(ldqc=128) == L.PF8_EINVAL
+    assert _qd(ld_sc=256) == L.PF8_EINVAL
+    assert _qd(x=A16 + 2) == L.PF8_EALIGN
+    assert _qd(qr=B16 + 8) == L.PF8_EALIGN
+    assert _qd(qc=C16 + 4) == L.PF8_EALIGN
+    assert _qd(sc=S4 + 2) == L.PF8_EALIGN
+    assert _qd(ldx=388) == L.PF8_EALIGN  # 776-byte pitch
+    assert _qd(ldqc=264) == L.PF8_EALIGN
 
 
 def _qw(**kw):
@@ -145,6 +173,7 @@ def test_no_device_is_reported_after_validation():
     assert _qw(qt=0, ldqt=0) == L.PF8_ENODEV  # no transposed copy requested
     assert _gm(m=1, n=3, ld_as=1, ldd=8) == L.PF8_ENODEV  # ragged M and N are accepted
     assert _qa() == L.PF8_ENODEV
+    assert _qd() == L.PF8_ENODEV
     assert _qw() == L.PF8_ENODEV
     assert _gm() == L.PF8_ENODEV
     assert L.pf8_block_gemm(L.PF8_WGRAD, 256, 384, 512, A16, 512, S4, 256, B16, 512, S4, 1, 4, C16, 384, 0) == \

@@ -143,3 +143,88 @@ def test_repeat_runs_are_bitwise_identical():
     torch.cuda.synchronize()
     for q, s in a[1:]:
         assert torch.equal(q, a[0][0]) and torch.equal(s, a[0][1])
+
+
+# ---- dual-orientation quantiser: one read, both groupings, bit-identical to the two passes ----
+
+def _check_dual(bits):
+    qr, sr, qc, sc = pf8.quant_act_dual(to_dev_bf16(bits))
+    torch.cuda.synchronize()
+    qr_ref, sr_ref = oracle.quant_act_1x128(bits, "cols")
+    qc_ref, sc_ref = oracle.quant_act_1x128(bits, "rows")
+    for got, ref, what in ((u8(qr), qr_ref, "row codes"), (u8(qc), qc_ref, "col codes")):
+        assert got.shape == ref.shape, what
+        bad = np.count_nonzero(got != ref)
+        assert bad == 0, f"{what}: {bad} mismatches, first at {np.argwhere(got != ref)[:5].tolist()}"
+    assert np.array_equal(f32(sr).view(np.uint32), sr_ref.view(np.uint32))
+    assert np.array_equal(f32(sc).view(np.uint32), sc_ref.view(np.uint32))
+
+
+def test_dual_every_bf16_pattern():
+    b = _every_bf16_pattern(512)
+    b = np.concatenate([b, b[:1]], 0)[:128]
+    _check_dual(np.ascontiguousarray(b))
+    _check_dual(np.ascontiguousarray(b.reshape(256, 256)[:, ::-1]))
+
+
+def test_dual_special_values():
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((256, 512)) * 0.3).astype(np.float32)
+    x[0, :128] = 0.0
+    x[1, :128] = -0.0
+    x[:128, 200] = 0.0                      # an all-zero column group
+    x[128:, 300] = -0.0
+    x[2, :128] = np.float32(2.0 ** -133)
+    x[3, :128] = np.float32(-3.3895314e38)
+    x[:128, 400] = np.float32(448.0)
+    x[128:, 401] = 450.0
+    x[6, 256:384] *= np.float32(1e-30)
+    x[7, :] = np.float32(2.0 ** -140)
+    _check_dual(f32_to_bf16_bits(x))
+
+
+@pytest.mark.parametrize("key,name", [("tiny_fprop", "X"), ("wgrad", "dY"), ("mlp_gateup_layer_step", "X")])
+def test_dual_workloads(key, name):
+    _check_dual(generate(key, only=[name])[name])
+
+
+@pytest.mark.parametrize("rows,cols", [(128, 128), (384, 256), (256, 1152)])
+def test_dual_matches_single_orientation_kernels(rows, cols):
+    rng = np.random.default_rng(rows + cols)
+    x = to_dev_bf16(f32_to_bf16_bits((rng.standard_normal((rows, cols)) * 5).astype(np.float32)))
+    qr, sr, qc, sc = pf8.quant_act_dual(x)
+    qr1, sr1 = pf8.quant_act_1x128(x, "cols")
+    qc1, sc1 = pf8.quant_act_1x128(x, "rows")
+    torch.cuda.synchronize()
+    assert torch.equal(qr, qr1) and torch.equal(qc, qc1)
+    assert torch.equal(sr.view(torch.int32), sr1.view(torch.int32))
+    assert torch.equal(sc.view(torch.int32), sc1.view(torch.int32))
+
+
+def test_dual_strided_inputs_and_untouched_padding():
+    rng = np.random.default_rng(11)
+    bits = f32_to_bf16_bits(rng.standard_normal((256, 384)).astype(np.float32))
+    big = np.zeros((256, 520), np.uint16)
+    big[:, :384] = bits
+    x = to_dev_bf16(big)[:, :384]
+    qr = torch.full((256, 400), 0xA5, dtype=torch.uint8, device=DEV)
+    sr = torch.full((3, 264), -7.0, dtype=torch.float32, device=DEV)
+    qc = torch.full((384, 272), 0x5A, dtype=torch.uint8, device=DEV)
+    sc = torch.full((2, 392), -3.0, dtype=torch.float32, device=DEV)
+    pf8._lib.check(pf8.pf8_quant_act_dual(x.data_ptr(), 256, 384, 520, qr.data_ptr(), 400, sr.data_ptr(), 264,
+                                          qc.data_ptr(), 272, sc.data_ptr(), 392,
+                                          torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    qr_ref, sr_ref = oracle.quant_act_1x128(bits, "cols")
+    qc_ref, sc_ref = oracle.quant_act_1x128(bits, "rows")
+    gqr, gsr, gqc, gsc = u8(qr), f32(sr), u8(qc), f32(sc)
+    assert np.array_equal(gqr[:, :384], qr_ref) and np.all(gqr[:, 384:] == 0xA5)
+    assert np.array_equal(gsr[:, :256], sr_ref) and np.all(gsr[:, 256:] == -7.0)
+    assert np.array_equal(gqc[:, :256], qc_ref) and np.all(gqc[:, 256:] == 0x5A)
+    assert np.array_equal(gsc[:, :384], sc_ref) and np.all(gsc[:, 384:] == -3.0)
+
+
+def test_dual_rejects_ragged_shapes():
+    x = torch.zeros((200, 256), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(RuntimeError, match="unsupported shape"):
+        pf8.quant_act_dual(x)
