@@ -49,9 +49,10 @@ def parse_args():
     ap.add_argument("--unfused", action="store_true", help="one quantiser pass per orientation (eight launches)")
     ap.add_argument("--no-configs", action="store_true", help="skip timing the per-configuration GEMMs")
     ap.add_argument("--no-comparators", action="store_true", help="skip timing hipBLASLt on the fprop shape")
-    ap.add_argument("--only", choices=["fprop_gemm", "copy"], default=None,
-                    help="profiling modes: run only the headline fprop GEMM, or only a 1 GiB device copy "
-                         "(the calibration kernel for the FETCH_SIZE / WRITE_SIZE counters), --steps times")
+    ap.add_argument("--only", choices=["fprop_gemm", "quant_dy_dual", "copy"], default=None,
+                    help="profiling modes: run only the headline fprop GEMM, only the dual-orientation dY "
+                         "quantiser, or only a 1 GiB device copy (the calibration kernel for the FETCH_SIZE / "
+                         "WRITE_SIZE counters), --steps times")
     ap.add_argument("--summarize-prof", nargs="+", metavar="DIR", default=None,
                     help="print a text summary of rocprofv3 csv output directories and exit")
     return ap.parse_args()
@@ -246,6 +247,14 @@ def only_mode(args, torch, pf8):
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"only": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                          "launches": args.steps}), flush=True)
+        return
+    if args.only == "quant_dy_dual":
+        dy = _dev_bf16(generate(WORKLOAD, only=["dY"])["dY"], torch)
+        for _ in range(args.steps):
+            pf8.quant_act_dual(dy)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "quant_dy_dual", "rows": dy.shape[0], "cols": dy.shape[1],
                           "launches": args.steps}), flush=True)
         return
     t = generate(WORKLOAD, only=["X", "W"])

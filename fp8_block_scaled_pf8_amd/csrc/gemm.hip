@@ -364,15 +364,16 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   constexpr int A_ST = BM * BK, ST = (BM + BN) * BK;
   constexpr int A_DMA = BM / 64, B_DMA = BN / 64, D = A_DMA + B_DMA;  // loads per wave per stage
   static_assert(NST == 2 || NST == 4 || NST == 5, "two, four or five stage buffers");
-  // at least four buffers: the epilogue stages the BM x BN output tile (64 rows per buffer) through them
+  // at least four buffers: the epilogue stages the BM x BN output tile through them
   constexpr int NBUF = NST < 4 ? 4 : NST;
   __shared__ __align__(16) uint8_t buf0[ST];
   __shared__ __align__(16) uint8_t buf1[ST];
   __shared__ __align__(16) uint8_t buf2[ST];
   __shared__ __align__(16) uint8_t buf3[ST];
   __shared__ __align__(16) uint8_t buf4[NBUF > 4 ? ST : 16];
-  static_assert(64 * BN * 2 <= ST, "64 output rows fit a stage buffer");
-  static_assert(BM <= 256, "at most four 64-row output slabs");
+  // the epilogue stages the output tile through the stage buffers, RPB rows per buffer
+  constexpr int RPB = (ST / (BN * 2)) < 64 ? (ST / (BN * 2)) : 64;
+  static_assert((BM + RPB - 1) / RPB <= NBUF, "the output tile fits the stage buffers");
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: keeps LDS and buffer offsets scalar
@@ -647,7 +648,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
 
   // ---- epilogue: BF16 tile staged through LDS, then written as whole rows ----
   // Lane owns D[m][n .. n+3], m = lane%32 of the MFMA tile, n = 8*(r/4) + 4*(lane/32). Row m of the
-  // tile goes to buffer m/64; its 16-byte chunk c sits at chunk phys(m, c) so that the 32 rows a
+  // tile goes to buffer m/RPB; its 16-byte chunk c sits at chunk phys(m, c) so that the 32 rows a
   // wave writes at once spread over the banks, and a wave then reads 16-byte chunks of whole rows
   // back and stores them contiguously (a 512-byte row per 32 lanes for BN = 256).
   constexpr int CH = BN / 8;  // 16-byte chunks per output row
@@ -660,7 +661,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int row = wm * WM + 32 * i + l32;
-    uint8_t* rb = bufs(row >> 6) + (row & 63) * RP;
+    uint8_t* rb = bufs(static_cast<unsigned>(row) / RPB) + (static_cast<unsigned>(row) % RPB) * RP;
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -677,7 +678,8 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   for (int it = 0; it < PER_T; ++it) {
     const int q = t + 256 * it;
     const int row = q / CH, c = q % CH;
-    const uint4 v = *reinterpret_cast<const uint4*>(bufs(row >> 6) + (row & 63) * RP + phys(row, c) * 16);
+    const uint4 v = *reinterpret_cast<const uint4*>(bufs(static_cast<unsigned>(row) / RPB) +
+                                                    (static_cast<unsigned>(row) % RPB) * RP + phys(row, c) * 16);
     const int64_t m = m0 + row, n = n0 + 8 * c;
     uint16_t* dst = p.d + m * p.ldd + n;
     if (!EDGE) {
@@ -729,25 +731,41 @@ static hipError_t launch_tile(const GemmArgs& args, bool row_b, hipStream_t stre
   return row_b ? launch_tile<BM, BN, true, MX>(args, stream) : launch_tile<BM, BN, false, MX>(args, stream);
 }
 
-// Macro-tile choice (MX variant): 256x256 unless that leaves the 256 CUs badly under-filled, in
-// which case a 256x192 tile may even out the last wave (e.g. the 2048x6144 wgrad: 192 tiles of
-// 256x256 but exactly 256 of 256x192). Small problems use 128-row tiles. The PROMOTE variant keeps
-// an extra FP32 partial per MFMA in flight and uses 256x128 tiles to stay within registers.
+// Macro-tile choice (MX variant). A launch takes ceil(tiles / 256) rounds of one tile per CU, so
+// its time is modelled as rounds x (tile area / relative per-flop efficiency of the tile shape),
+// and the cheapest shape wins. Smaller tiles re-read more operand bytes per flop (efficiency
+// below 1) but can fill the 256 CUs evenly: the 12288x2048 weight gradient is 384 tiles of
+// 256x256 (1.5 rounds) but exactly 512 of 192x256 (2 rounds of 3/4 the work), the 2048x6144 one
+// 192 tiles of 256x256 but 256 of 256x192. The PROMOTE variant keeps an extra FP32 partial per
+// MFMA in flight and uses 256x128 tiles to stay within registers.
 hipError_t launch_gemm(const GemmArgs& args, bool row_b_scale, bool mx, hipStream_t stream) {
   if (!mx) {
     if (args.m >= 256) return launch_tile<256, 128, false>(args, row_b_scale, stream);
     return launch_tile<128, 128, false>(args, row_b_scale, stream);
   }
-  auto fill = [&](int bm, int bn) {
-    const int64_t t = ((args.m + bm - 1) / bm) * ((args.n + bn - 1) / bn), waves = (t + 255) / 256;
-    return static_cast<double>(t) / static_cast<double>(waves * 256);
+  struct Shape {
+    int bm, bn;
+    double eff;
   };
-  const double f256 = fill(256, 256), f192 = fill(256, 192);
-  if (args.m >= 256 && args.n >= 256 && f256 >= 0.9) return launch_tile<256, 256, true>(args, row_b_scale, stream);
-  if (args.m >= 256 && args.n >= 192 && f192 > f256) return launch_tile<256, 192, true>(args, row_b_scale, stream);
-  if (args.m >= 256 && args.n >= 256) return launch_tile<256, 256, true>(args, row_b_scale, stream);
-  if (args.m >= 256) return launch_tile<256, 128, true>(args, row_b_scale, stream);
-  return launch_tile<128, 128, true>(args, row_b_scale, stream);
+  constexpr Shape kShapes[] = {{256, 256, 1.0}, {256, 192, 0.95}, {192, 256, 0.95}, {256, 128, 0.85}, {128, 128, 0.7}};
+  int best = 0;
+  double best_cost = 0.0;
+  for (int i = 0; i < static_cast<int>(sizeof(kShapes) / sizeof(kShapes[0])); ++i) {
+    const Shape& sh = kShapes[i];
+    const int64_t tiles = ((args.m + sh.bm - 1) / sh.bm) * ((args.n + sh.bn - 1) / sh.bn);
+    const double cost = static_cast<double>((tiles + 255) / 256) * sh.bm * sh.bn / sh.eff;
+    if (i == 0 || cost < best_cost) {
+      best = i;
+      best_cost = cost;
+    }
+  }
+  switch (best) {
+    case 0: return launch_tile<256, 256, true>(args, row_b_scale, stream);
+    case 1: return launch_tile<256, 192, true>(args, row_b_scale, stream);
+    case 2: return launch_tile<192, 256, true>(args, row_b_scale, stream);
+    case 3: return launch_tile<256, 128, true>(args, row_b_scale, stream);
+    default: return launch_tile<128, 128, true>(args, row_b_scale, stream);
+  }
 }
 
 }  // namespace pf8
