@@ -23,7 +23,7 @@ PF8_OK, PF8_EINVAL, PF8_ESHAPE, PF8_EALIGN, PF8_ENODEV, PF8_ELAUNCH = range(6)
 PF8_ALONG_COLS, PF8_ALONG_ROWS = 0, 1
 PF8_FPROP, PF8_DGRAD, PF8_WGRAD = 0, 1, 2
 PF8_GEMM_AUTO, PF8_GEMM_MX_SCALED, PF8_GEMM_PROMOTE = 0, 1, 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
@@ -37,6 +37,8 @@ SIGNATURES = {
     "pf8_block_gemm": (_int, [_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
     "pf8_block_gemm_variant": (
         _int, [_int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
+    "pf8_block_gemm_f32": (
+        _int, [_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _int, _vp]),
     "pf8_strerror": (ctypes.c_char_p, [_int]),
     "pf8_abi_version": (_int, []),
 }
@@ -84,6 +86,12 @@ def pf8_block_gemm_variant(variant, layout, m, n, k, a, lda, a_dscale, ld_as, b,
                            ldd, hip_stream=0) -> int:
     return LIB.pf8_block_gemm_variant(variant, layout, m, n, k, a, lda, a_dscale, ld_as, b, ldb, b_dscale, sb_n,
                                       sb_k, d, ldd, hip_stream)
+
+
+def pf8_block_gemm_f32(layout, m, n, k, a, lda, a_dscale, ld_as, b, ldb, b_dscale, sb_n, sb_k, d, ldd, accumulate,
+                       hip_stream=0) -> int:
+    return LIB.pf8_block_gemm_f32(layout, m, n, k, a, lda, a_dscale, ld_as, b, ldb, b_dscale, sb_n, sb_k, d, ldd,
+                                  accumulate, hip_stream)
 
 
 def pf8_strerror(status: int) -> str:

@@ -113,9 +113,28 @@ int pf8_block_gemm_variant(int variant, int layout, int64_t m, int64_t n, int64_
   if ((m + 127) / 128 * ((n + 127) / 128) > (int64_t{1} << 31) - 1) return PF8_ESHAPE;
   if (int s = device_status(); s != PF8_OK) return s;
   pf8::GemmArgs args{m, n, k, static_cast<const uint8_t*>(a), lda, a_dscale, ld_as, static_cast<const uint8_t*>(b),
-                     ldb, b_dscale, sb_n, sb_k, static_cast<uint16_t*>(d), ldd};
+                     ldb, b_dscale, sb_n, sb_k, static_cast<uint16_t*>(d), ldd, nullptr, 0};
   const bool mx = variant != PF8_GEMM_PROMOTE;
   return launch_status(pf8::launch_gemm(args, layout == PF8_WGRAD, mx, static_cast<hipStream_t>(hip_stream)));
+}
+
+int pf8_block_gemm_f32(int layout, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const float* a_dscale,
+                       int64_t ld_as, const void* b, int64_t ldb, const float* b_dscale, int64_t sb_n, int64_t sb_k,
+                       float* d, int64_t ldd, int accumulate, void* hip_stream) {
+  if (layout != PF8_FPROP && layout != PF8_DGRAD && layout != PF8_WGRAD) return PF8_EINVAL;
+  if (accumulate != 0 && accumulate != 1) return PF8_EINVAL;
+  if (a == nullptr || b == nullptr || d == nullptr || a_dscale == nullptr || b_dscale == nullptr) return PF8_EINVAL;
+  if (m <= 0 || n <= 0 || k <= 0) return PF8_EINVAL;
+  if (k % kGroup != 0) return PF8_ESHAPE;
+  if (lda < k || ldb < k || ldd < n || ld_as < m || sb_n < 1 || sb_k < 1) return PF8_EINVAL;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(d) || !aligned4(a_dscale) || !aligned4(b_dscale)) return PF8_EALIGN;
+  if (lda % 16 != 0 || ldb % 16 != 0 || (ldd * 4) % 16 != 0) return PF8_EALIGN;
+  if (lda > kMaxTilePitch || ldb > kMaxTilePitch) return PF8_ESHAPE;
+  if ((m + 127) / 128 * ((n + 127) / 128) > (int64_t{1} << 31) - 1) return PF8_ESHAPE;
+  if (int s = device_status(); s != PF8_OK) return s;
+  pf8::GemmArgs args{m, n, k, static_cast<const uint8_t*>(a), lda, a_dscale, ld_as, static_cast<const uint8_t*>(b),
+                     ldb, b_dscale, sb_n, sb_k, nullptr, ldd, d, accumulate};
+  return launch_status(pf8::launch_gemm(args, layout == PF8_WGRAD, true, static_cast<hipStream_t>(hip_stream)));
 }
 
 int pf8_block_gemm(int layout, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const float* a_dscale,

@@ -357,7 +357,7 @@ __device__ __forceinline__ void interleave_groups() {
 //    a fixed LDS object and the compiler can track each buffer's direct-to-LDS loads separately.
 //  * The block scales of a stage travel with its operands: they are loaded into the scale registers
 //    of the stage's buffer when the stage is issued, NST stages before use.
-template <int BM, int BN, bool ROW_B, bool EDGE, int NST>
+template <int BM, int BN, bool ROW_B, bool EDGE, int NST, bool F32 = false>
 __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, int tiles_n) {
   constexpr int BK = 64;
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
@@ -646,6 +646,40 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   }
 #undef PF8_WAIT_VM_LGKM0
 
+  if constexpr (F32) {
+    // ---- epilogue, FP32 result: straight from the accumulators ----
+    // Lane owns D[m][n .. n+3] (16 bytes), m = row l%32 of the MFMA tile, n = 8*(r/4) + 4*(l/32);
+    // with accumulate, the old value is read and the sum written back (one owner per element).
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t m = m0 + wm * WM + 32 * i + l32;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int64_t n = n0 + wn * WN + 32 * j + 8 * q4 + 4 * half;
+          float* dst = p.d32 + m * p.ldd + n;
+          float4 v = make_float4(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
+                                 acc[i][j][4 * q4 + 3]);
+          if (!EDGE || (m < M && n + 3 < N)) {
+            if (p.accumulate) {
+              const float4 o = *reinterpret_cast<const float4*>(dst);
+              v = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+            }
+            *reinterpret_cast<float4*>(dst) = v;
+          } else if (m < M) {
+            const float w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) dst[e] = p.accumulate ? dst[e] + w[e] : w[e];
+          }
+        }
+      // keep the read-modify-write of one 32-row slab in flight at a time (registers)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return;
+  }
+
   // ---- epilogue: BF16 tile staged through LDS, then written as whole rows ----
   // Lane owns D[m][n .. n+3], m = lane%32 of the MFMA tile, n = 8*(r/4) + 4*(lane/32). Row m of the
   // tile goes to buffer m/RPB; its 16-byte chunk c sits at chunk phys(m, c) so that the 32 rows a
@@ -704,17 +738,24 @@ static hipError_t launch_tile(const GemmArgs& args, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n)), block(256);
   const bool edge = args.m % BM != 0 || args.n % BN != 0;
   if constexpr (MX) {
-    // deepest pipeline that fits the 160 KB LDS and the K extent
-    constexpr int kMaxNst = 5 * (BM + BN) * 64 <= 160 * 1024 ? 5 : 4;
+    // five stage buffers fit the 160 KB LDS for every tile shape here; K extents under five
+    // stages take the two-buffer pipeline
+    static_assert(5 * (BM + BN) * 64 <= 160 * 1024, "five stage buffers fit the LDS");
     const int64_t ns = args.k / 64;
-    const int nst = ns >= kMaxNst ? kMaxNst : (ns >= 4 ? 4 : 2);
-    if (edge) {
-      if (nst == 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, kMaxNst>), grid, block, 0, stream, args, tiles_m, tiles_n);
-      else if (nst == 4) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 4>), grid, block, 0, stream, args, tiles_m, tiles_n);
+    // FP32 results (three tile shapes only): one edge-checked kernel per pipeline depth
+    constexpr bool kF32Tile = (BM == 256 && BN == 256) || (BM == 192 && BN == 256) || (BM == 128 && BN == 128);
+    if (args.d32 != nullptr) {
+      if constexpr (kF32Tile) {
+        if (ns >= 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 5, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
+        else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 2, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
+      } else {
+        return hipErrorInvalidValue;  // not reached: the FP32 tile choice offers only the shapes above
+      }
+    } else if (edge) {
+      if (ns >= 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 5>), grid, block, 0, stream, args, tiles_m, tiles_n);
       else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 2>), grid, block, 0, stream, args, tiles_m, tiles_n);
     } else {
-      if (nst == 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, false, kMaxNst>), grid, block, 0, stream, args, tiles_m, tiles_n);
-      else if (nst == 4) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, false, 4>), grid, block, 0, stream, args, tiles_m, tiles_n);
+      if (ns >= 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, false, 5>), grid, block, 0, stream, args, tiles_m, tiles_n);
       else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, false, 2>), grid, block, 0, stream, args, tiles_m, tiles_n);
     }
   } else {
@@ -737,7 +778,7 @@ static hipError_t launch_tile(const GemmArgs& args, bool row_b, hipStream_t stre
 // below 1) but can fill the 256 CUs evenly: the 12288x2048 weight gradient is 384 tiles of
 // 256x256 (1.5 rounds) but exactly 512 of 192x256 (2 rounds of 3/4 the work), the 2048x6144 one
 // 192 tiles of 256x256 but 256 of 256x192. The PROMOTE variant keeps an extra FP32 partial per
-// MFMA in flight and uses 256x128 tiles to stay within registers.
+// MFMA in flight and uses 256x128 tiles to stay within registers; it has no FP32-output form.
 hipError_t launch_gemm(const GemmArgs& args, bool row_b_scale, bool mx, hipStream_t stream) {
   if (!mx) {
     if (args.m >= 256) return launch_tile<256, 128, false>(args, row_b_scale, stream);
@@ -748,9 +789,11 @@ hipError_t launch_gemm(const GemmArgs& args, bool row_b_scale, bool mx, hipStrea
     double eff;
   };
   constexpr Shape kShapes[] = {{256, 256, 1.0}, {256, 192, 0.95}, {192, 256, 0.95}, {256, 128, 0.85}, {128, 128, 0.7}};
+  const bool f32 = args.d32 != nullptr;  // FP32 results are built for shapes 0, 2 and 4
   int best = 0;
   double best_cost = 0.0;
   for (int i = 0; i < static_cast<int>(sizeof(kShapes) / sizeof(kShapes[0])); ++i) {
+    if (f32 && (i == 1 || i == 3)) continue;
     const Shape& sh = kShapes[i];
     const int64_t tiles = ((args.m + sh.bm - 1) / sh.bm) * ((args.n + sh.bn - 1) / sh.bn);
     const double cost = static_cast<double>((tiles + 255) / 256) * sh.bm * sh.bn / sh.eff;

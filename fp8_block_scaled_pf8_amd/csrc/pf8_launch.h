@@ -26,8 +26,10 @@ struct GemmArgs {
   int64_t ldb;
   const float* b_dscale;
   int64_t sb_n, sb_k;
-  uint16_t* d;
+  uint16_t* d;     // BF16 output (when d32 is null)
   int64_t ldd;
+  float* d32;      // FP32 output instead of d, or null
+  int accumulate;  // with d32: add the product to d32's contents instead of overwriting them
 };
 
 // row_b_scale: B's scales are per (K-block, row) (wgrad) instead of per 128x128 tile.

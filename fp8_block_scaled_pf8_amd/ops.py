@@ -115,6 +115,36 @@ def block_gemm(layout: int, a: torch.Tensor, a_dscale: torch.Tensor, b: torch.Te
     return out
 
 
+def block_gemm_f32(layout: int, a: torch.Tensor, a_dscale: torch.Tensor, b: torch.Tensor, b_dscale: torch.Tensor,
+                   sb_n: int, sb_k: int, out: Optional[torch.Tensor] = None, accumulate: bool = False
+                   ) -> torch.Tensor:
+    """D[m, n] (+)= sum_k deq(A)[m, k] deq(B)[n, k] in FP32 (see pf8_block_gemm_f32 in include/pf8.h).
+
+    With ``accumulate`` the product is added to ``out`` (required), otherwise ``out`` is overwritten
+    (or allocated)."""
+    _check_2d(a, torch.uint8, "a")
+    _check_2d(b, torch.uint8, "b")
+    _check_2d(a_dscale, torch.float32, "a_dscale")
+    if b_dscale.dtype != torch.float32 or not b_dscale.is_cuda:
+        raise TypeError("b_dscale must be a float32 device tensor")
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k:
+        raise ValueError(f"reduction dims differ: a {tuple(a.shape)}, b {tuple(b.shape)}")
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an output tensor to add to")
+        pitch = (n + 3) // 4 * 4  # 16-byte row pitch
+        out = torch.empty((m, pitch), dtype=torch.float32, device=a.device)[:, :n]
+    _check_2d(out, torch.float32, "out")
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out has the wrong shape")
+    L.check(L.pf8_block_gemm_f32(layout, m, n, k, a.data_ptr(), a.stride(0), a_dscale.data_ptr(), a_dscale.stride(0),
+                                 b.data_ptr(), b.stride(0), b_dscale.data_ptr(), sb_n, sb_k, out.data_ptr(),
+                                 out.stride(0), int(accumulate), _stream(a)), "pf8_block_gemm_f32")
+    return out
+
+
 def fprop(qx, sx, qw, sw, out=None, variant: int = L.PF8_GEMM_AUTO) -> torch.Tensor:
     """Y = X . W^T from row-mode X codes and W tile codes."""
     return block_gemm(L.PF8_FPROP, qx, sx, qw, sw, sw.stride(0), 1, out, variant)
@@ -128,6 +158,11 @@ def dgrad(qdy, sdy, qwt, sw, out=None, variant: int = L.PF8_GEMM_AUTO) -> torch.
 def wgrad(qdyt, sdy, qxt, sx, out=None, variant: int = L.PF8_GEMM_AUTO) -> torch.Tensor:
     """dW = dY^T . X from col-mode (token-grouped) dY and X codes."""
     return block_gemm(L.PF8_WGRAD, qdyt, sdy, qxt, sx, 1, sx.stride(0), out, variant)
+
+
+def wgrad_f32(qdyt, sdy, qxt, sx, out=None, accumulate: bool = False) -> torch.Tensor:
+    """dW = dY^T . X in FP32; with ``accumulate``, dW is added to ``out`` (an FP32 main gradient)."""
+    return block_gemm_f32(L.PF8_WGRAD, qdyt, sdy, qxt, sx, 1, sx.stride(0), out, accumulate)
 
 
 class LinearStep:

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define PF8_ABI_VERSION 2
+#define PF8_ABI_VERSION 3
 
 /* Status codes (int). */
 #define PF8_OK 0
@@ -135,6 +135,25 @@ int pf8_block_gemm_variant(int variant, int layout, int64_t m, int64_t n, int64_
                            const void* a, int64_t lda, const float* a_dscale, int64_t ld_as,
                            const void* b, int64_t ldb, const float* b_dscale, int64_t sb_n, int64_t sb_k,
                            void* d, int64_t ldd, void* hip_stream);
+
+/*
+ * Block-scaled FP8 GEMM with an FP32 result [paperlayer.ai summary, appendix C "Production
+ * Training Details": gradients are kept in FP32; with several micro-batches per optimizer step
+ * the weight gradient is a running FP32 sum]:
+ *
+ *   accumulate = 0:  D[i, j]  = sum_kb sa(kb, i) * sb(kb, j) * sum_{k in block kb} decode(A[i, k]) * decode(B[j, k])
+ *   accumulate = 1:  D[i, j] += (the same sum)
+ *
+ * Layouts, operands, scales and limits are exactly those of pf8_block_gemm; the product is formed
+ * by the MX-scaled kernel with FP32 accumulation and is not rounded to BF16.
+ * d: f32 [m, n], row pitch ldd >= n with ldd * 4 a multiple of 16 bytes, 16-byte aligned base.
+ * With accumulate = 1 every element of d is read once and written once by a single thread (no
+ * atomics); d must not overlap a or b. accumulate other than 0 or 1 is PF8_EINVAL.
+ */
+int pf8_block_gemm_f32(int layout, int64_t m, int64_t n, int64_t k,
+                       const void* a, int64_t lda, const float* a_dscale, int64_t ld_as,
+                       const void* b, int64_t ldb, const float* b_dscale, int64_t sb_n, int64_t sb_k,
+                       float* d, int64_t ldd, int accumulate, void* hip_stream);
 
 /* Static, NUL-terminated description of a status code ("unknown status" for other values). */
 const char* pf8_strerror(int status);

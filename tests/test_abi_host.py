@@ -26,7 +26,7 @@ def _declared_functions():
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
     assert names == sorted(["pf8_quant_act_1x128", "pf8_quant_act_dual", "pf8_quant_w_128x128", "pf8_block_gemm",
-                            "pf8_block_gemm_variant", "pf8_strerror", "pf8_abi_version"])
+                            "pf8_block_gemm_variant", "pf8_block_gemm_f32", "pf8_strerror", "pf8_abi_version"])
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -162,6 +162,31 @@ def test_gemm_validation():
     assert _gm(lda=1 << 24, ldb=1 << 24) == L.PF8_ESHAPE  # pitch beyond the 32-bit tile offset range
 
 
+def _gf(**kw):
+    a = dict(layout=L.PF8_WGRAD, m=256, n=384, k=512, a=A16, lda=512, a_dscale=S4, ld_as=256, b=B16, ldb=512,
+             b_dscale=S4, sb_n=1, sb_k=384, d=C16, ldd=384, accumulate=1)
+    a.update(kw)
+    return L.pf8_block_gemm_f32(a["layout"], a["m"], a["n"], a["k"], a["a"], a["lda"], a["a_dscale"], a["ld_as"],
+                                a["b"], a["ldb"], a["b_dscale"], a["sb_n"], a["sb_k"], a["d"], a["ldd"],
+                                a["accumulate"], 0)
+
+
+def test_gemm_f32_validation():
+    assert _gf(layout=5) == L.PF8_EINVAL
+    assert _gf(accumulate=2) == L.PF8_EINVAL
+    assert _gf(accumulate=-1) == L.PF8_EINVAL
+    for key in ["a", "b", "d", "a_dscale", "b_dscale"]:
+        assert _gf(**{key: 0}) == L.PF8_EINVAL, key
+    assert _gf(m=0) == L.PF8_EINVAL
+    assert _gf(k=200, lda=512, ldb=512) == L.PF8_ESHAPE
+    assert _gf(ldd=300) == L.PF8_EINVAL
+    assert _gf(ld_as=128) == L.PF8_EINVAL
+    assert _gf(d=C16 + 8) == L.PF8_EALIGN
+    assert _gf(ldd=386) == L.PF8_EALIGN  # 1544-byte pitch
+    assert _gf(a=A16 + 4) == L.PF8_EALIGN
+    assert _gf(lda=1 << 24, ldb=1 << 24) == L.PF8_ESHAPE
+
+
 def test_no_device_is_reported_after_validation():
     # valid arguments pass validation and then find no device; with a GPU present these fake
     # addresses would reach a kernel, so this runs only where there is none
@@ -174,6 +199,8 @@ def test_no_device_is_reported_after_validation():
     assert _gm(m=1, n=3, ld_as=1, ldd=8) == L.PF8_ENODEV  # ragged M and N are accepted
     assert _qa() == L.PF8_ENODEV
     assert _qd() == L.PF8_ENODEV
+    assert _gf() == L.PF8_ENODEV
+    assert _gf(accumulate=0, m=3, n=5, ld_as=3, ldd=8) == L.PF8_ENODEV
     assert _qw() == L.PF8_ENODEV
     assert _gm() == L.PF8_ENODEV
     assert L.pf8_block_gemm(L.PF8_WGRAD, 256, 384, 512, A16, 512, S4, 256, B16, 512, S4, 1, 4, C16, 384, 0) == \

@@ -326,3 +326,77 @@ def test_layer_step_workload_sampled():
     qxt, sxt = oracle.quant_act_1x128(t["X"], "rows")
     assert np.array_equal(u8(step.qdyt)[cols], qdyt) and np.array_equal(u8(step.qxt), qxt)
     _report(bf16_f64(step.dw)[cols], oracle.gemm_wgrad(qdyt, sdyt, qxt, sxt), "layer wgrad")
+
+
+# ---- FP32 results (pf8_block_gemm_f32): same products, no BF16 rounding, optional accumulate ----
+
+def _operands(layout, m, n, k, seed):
+    """Oracle codes and scales for one layout, as (a, sa, b, sb, sb_n, sb_k, ref64)."""
+    if layout == pf8.PF8_WGRAD:
+        dyt = _rand_bits((k, m + (-m % 8)), seed, 1e-3, outliers=False)
+        xt = _rand_bits((k, n + (-n % 8)), seed + 1)
+        qa, sa = oracle.quant_act_1x128(dyt, "rows")
+        qb, sb = oracle.quant_act_1x128(xt, "rows")
+        ref = oracle.gemm_wgrad(qa[:m], sa[:, :m], qb[:n], sb[:, :n])
+        return qa[:m], sa, qb[:n], sb, 1, sb.shape[1], ref
+    n_pad = (n + 127) // 128 * 128
+    if layout == pf8.PF8_FPROP:
+        qa, sa = oracle.quant_act_1x128(_rand_bits((m, k), seed), "cols")
+        qw, _, sw = oracle.quant_w_128x128(_rand_bits((n_pad, k), seed + 1, 0.02, outliers=False))
+        return qa, sa, qw[:n], sw, sw.shape[1], 1, oracle.gemm_fprop(qa, sa, qw[:n], sw)
+    qa, sa = oracle.quant_act_1x128(_rand_bits((m, k), seed, 1e-3, outliers=False), "cols")
+    _, qwt, sw = oracle.quant_w_128x128(_rand_bits((k, n_pad), seed + 1, 0.01, outliers=False))
+    return qa, sa, qwt[:n], sw, 1, sw.shape[1], oracle.gemm_dgrad(qa, sa, qwt[:n], sw)
+
+
+LAYOUTS = {"fprop": pf8.PF8_FPROP, "dgrad": pf8.PF8_DGRAD, "wgrad": pf8.PF8_WGRAD}
+
+
+@pytest.mark.parametrize("lname", list(LAYOUTS))
+@pytest.mark.parametrize("m,n,k", [(1, 1, 128), (3, 130, 256), (257, 129, 384), (640, 448, 256), (2050, 5407, 384),
+                                   (1024, 1024, 640)])
+def test_gemm_f32_matches_oracle_and_bf16_path(lname, m, n, k):
+    layout = LAYOUTS[lname]
+    qa, sa, qb, sb, sb_n, sb_k, ref = _operands(layout, m, n, k, m + 3 * n + k)
+    a, sa_d, b, sb_d = to_dev_u8(qa), to_dev_f32(sa), to_dev_u8(qb), to_dev_f32(sb)
+    d32 = pf8.block_gemm_f32(layout, a, sa_d, b, sb_d, sb_n, sb_k)
+    d16 = pf8.block_gemm(layout, a, sa_d, b, sb_d, sb_n, sb_k, variant=pf8.PF8_GEMM_MX_SCALED)
+    torch.cuda.synchronize()
+    got = d32.cpu().numpy().astype(np.float64)
+    rep = oracle.gemm_tolerance_report(got, ref)  # (its BF16 bit-equality diagnostic is for BF16 outputs)
+    assert rep["violations"] == 0, f"f32 {lname} {m}x{n}x{k}: {rep}"
+    # the BF16 kernels hold the same FP32 accumulators: rounding the FP32 result reproduces them
+    assert np.array_equal(oracle.bf16_round_from_f64(got), bf16_bits(d16))
+
+
+@pytest.mark.parametrize("lname", ["wgrad", "fprop"])
+def test_gemm_f32_accumulates_into_output(lname):
+    layout = LAYOUTS[lname]
+    m, n, k = 384, 520, 512
+    qa, sa, qb, sb, sb_n, sb_k, _ = _operands(layout, m, n, k, 77)
+    a, sa_d, b, sb_d = to_dev_u8(qa), to_dev_f32(sa), to_dev_u8(qb), to_dev_f32(sb)
+    prod = pf8.block_gemm_f32(layout, a, sa_d, b, sb_d, sb_n, sb_k)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    base = torch.randn((m, n + 4), generator=g).to(DEV)[:, :n]  # padded pitch, 16-byte rows
+    pad_before = base.as_strided((m, 4), (n + 4, 1), n).clone()
+    start = base.clone()
+    pf8.block_gemm_f32(layout, a, sa_d, b, sb_d, sb_n, sb_k, out=base, accumulate=True)
+    pf8.block_gemm_f32(layout, a, sa_d, b, sb_d, sb_n, sb_k, out=base, accumulate=True)
+    torch.cuda.synchronize()
+    # two accumulations: ((start + p) + p) in FP32, element by element
+    assert torch.equal(base, (start + prod) + prod)
+    assert torch.equal(base.as_strided((m, 4), (n + 4, 1), n), pad_before)  # padding untouched
+
+
+def test_gemm_f32_validation_on_device():
+    a = torch.zeros((128, 128), dtype=torch.uint8, device=DEV)
+    s = torch.ones((1, 128), dtype=torch.float32, device=DEV)
+    st = torch.cuda.current_stream().cuda_stream
+    d = torch.zeros((128, 128), dtype=torch.float32, device=DEV)
+    args = (pf8.PF8_WGRAD, 128, 128, 128, a.data_ptr(), 128, s.data_ptr(), 128, a.data_ptr(), 128, s.data_ptr(), 1,
+            128, d.data_ptr(), 128)
+    assert pf8.pf8_block_gemm_f32(*args, 2, st) == pf8._lib.PF8_EINVAL
+    assert pf8.pf8_block_gemm_f32(*args[:-1], 130, 0, st) == pf8._lib.PF8_EALIGN  # 520-byte pitch
+    assert pf8.pf8_block_gemm_f32(*args, 0, st) == pf8._lib.PF8_OK
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(d) == 0

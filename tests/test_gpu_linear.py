@@ -1,0 +1,82 @@
+"""The FP8 linear layer under autograd (fp8_linear / Fp8Linear) against the CPU oracle.
+
+Forward Y, and backward dX and dW (BF16, or FP32 accumulated into a main gradient over several
+micro-batches), each compared element by element with the oracle's GEMM on the oracle's codes,
+to |gpu - ref| <= 2^-7 |ref| + 1e-3 rms(ref)."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_pf8_amd as pf8
+import oracle
+from workloads import f32_to_bf16_bits
+from tests.gpu_helpers import DEV, bf16_f64, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(shape, seed, sigma, outliers):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(shape) * sigma).astype(np.float32)
+    if outliers:
+        x.reshape(-1)[rng.choice(x.size, max(1, x.size // 200), replace=False)] *= 50
+    return f32_to_bf16_bits(x)
+
+
+def _check(gpu, ref, what):
+    rep = oracle.gemm_tolerance_report(gpu, ref)
+    assert rep["violations"] == 0, f"{what}: {rep}"
+
+
+def _oracle_layer(xb, wb, dyb):
+    qx, sx = oracle.quant_act_1x128(xb, "cols")
+    qxt, sxt = oracle.quant_act_1x128(xb, "rows")
+    qw, qwt, sw = oracle.quant_w_128x128(wb)
+    qdy, sdy = oracle.quant_act_1x128(dyb, "cols")
+    qdyt, sdyt = oracle.quant_act_1x128(dyb, "rows")
+    return (oracle.gemm_fprop(qx, sx, qw, sw), oracle.gemm_dgrad(qdy, sdy, qwt, sw),
+            oracle.gemm_wgrad(qdyt, sdyt, qxt, sxt))
+
+
+@pytest.mark.parametrize("batch,seq,k,n", [(2, 128, 512, 384), (1, 256, 256, 640)])
+def test_fp8_linear_forward_backward(batch, seq, k, n):
+    m = batch * seq
+    xb = _bits((m, k), 1 + k, 1.0, True)
+    wb = _bits((n, k), 2 + n, 0.02, False)
+    dyb = _bits((m, n), 3 + m, 1e-3, False)
+    x = to_dev_bf16(xb).reshape(batch, seq, k).requires_grad_(True)
+    w = to_dev_bf16(wb).requires_grad_(True)
+    y = pf8.fp8_linear(x, w)
+    assert y.shape == (batch, seq, n) and y.dtype == torch.bfloat16
+    y.backward(to_dev_bf16(dyb).reshape(batch, seq, n))
+    torch.cuda.synchronize()
+    ry, rdx, rdw = _oracle_layer(xb, wb, dyb)
+    _check(bf16_f64(y.detach().reshape(m, n)), ry, "Y")
+    _check(bf16_f64(x.grad.reshape(m, k)), rdx, "dX")
+    _check(bf16_f64(w.grad), rdw, "dW")
+
+
+def test_fp8_linear_fp32_main_grad_accumulates_micro_batches():
+    m, k, n = 256, 384, 512
+    layer = pf8.Fp8Linear(k, n, device=DEV, fp32_main_grad=True,
+                          weight=to_dev_bf16(_bits((n, k), 7, 0.02, False)))
+    wb = _bits((n, k), 7, 0.02, False)
+    want = np.zeros((n, k))
+    for mb in range(3):
+        xb = _bits((m, k), 10 + mb, 1.0, True)
+        dyb = _bits((m, n), 20 + mb, 1e-3, False)
+        x = to_dev_bf16(xb).requires_grad_(True)
+        y = layer(x)
+        y.backward(to_dev_bf16(dyb))
+        want += _oracle_layer(xb, wb, dyb)[2]
+    torch.cuda.synchronize()
+    assert layer.weight.grad is None
+    got = layer.weight.main_grad.cpu().numpy().astype(np.float64)
+    _check(got, want, "FP32 main_grad over 3 micro-batches")
+
+
+def test_fp8_linear_rejects_ragged_tokens():
+    x = torch.zeros((100, 256), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros((128, 256), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError, match="multiples of 128"):
+        pf8.fp8_linear(x, w)
