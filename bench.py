@@ -101,9 +101,10 @@ def run_step_timed(step, steps, torch):
     return [name for name, _ in launches], evs
 
 
-def time_comparators(torch, m, n, k, reps=20):
-    """hipBLASLt through torch on the fprop shape, as context: FP8 E4M3 with one scale per tensor
-    and per row / column (not block scales), and BF16."""
+def time_comparators(torch, pf8, m, n, k, reps=20):
+    """On the fprop shape, as context: this library's plain BF16 GEMM (same pipeline, BF16
+    operands), and hipBLASLt through torch: FP8 E4M3 with one scale per tensor and per row /
+    column (not block scales), and BF16."""
     dev = "cuda:0"
     g = torch.Generator(device=dev).manual_seed(0)
     a = (torch.randn(m, k, device=dev, generator=g) * 0.5).to(torch.float8_e4m3fn)
@@ -111,7 +112,9 @@ def time_comparators(torch, m, n, k, reps=20):
     one = torch.ones((), device=dev)
     sa, sb = torch.ones((m, 1), device=dev), torch.ones((1, n), device=dev)
     ab, bb = a.to(torch.bfloat16), b.to(torch.bfloat16).contiguous()
+    y16 = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
     cases = {
+        "libpf8_bf16": lambda: pf8.gemm_bf16(ab, bb, out=y16),
         "hipblaslt_fp8_tensorwise": lambda: torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one,
                                                              out_dtype=torch.bfloat16),
         "hipblaslt_fp8_rowwise": lambda: torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16),
@@ -133,7 +136,7 @@ def time_comparators(torch, m, n, k, reps=20):
             out[name] = {"us": round(us, 2), "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)}
         except Exception as ex:  # a comparator that torch cannot run is reported, not fatal
             out[name] = {"error": repr(ex)[:200]}
-    del a, b, ab, bb
+    del a, b, ab, bb, y16
     torch.cuda.empty_cache()
     return {"shape": [m, n, k], "note": "library GEMMs without block scales; context only", **out}
 
@@ -387,7 +390,7 @@ def main():
     if not args.no_configs:
         result["config_gemms"] = time_config_gemms(pf8, torch)
     if not args.no_comparators:
-        result["comparators"] = time_comparators(torch, m, n, k)
+        result["comparators"] = time_comparators(torch, pf8, m, n, k)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)

@@ -23,7 +23,7 @@ PF8_OK, PF8_EINVAL, PF8_ESHAPE, PF8_EALIGN, PF8_ENODEV, PF8_ELAUNCH = range(6)
 PF8_ALONG_COLS, PF8_ALONG_ROWS = 0, 1
 PF8_FPROP, PF8_DGRAD, PF8_WGRAD = 0, 1, 2
 PF8_GEMM_AUTO, PF8_GEMM_MX_SCALED, PF8_GEMM_PROMOTE = 0, 1, 2
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
@@ -39,6 +39,7 @@ SIGNATURES = {
         _int, [_int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
     "pf8_block_gemm_f32": (
         _int, [_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _int, _vp]),
+    "pf8_gemm_bf16": (_int, [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
     "pf8_strerror": (ctypes.c_char_p, [_int]),
     "pf8_abi_version": (_int, []),
 }
@@ -92,6 +93,10 @@ def pf8_block_gemm_f32(layout, m, n, k, a, lda, a_dscale, ld_as, b, ldb, b_dscal
                        hip_stream=0) -> int:
     return LIB.pf8_block_gemm_f32(layout, m, n, k, a, lda, a_dscale, ld_as, b, ldb, b_dscale, sb_n, sb_k, d, ldd,
                                   accumulate, hip_stream)
+
+
+def pf8_gemm_bf16(m, n, k, a, lda, b, ldb, d, ldd, hip_stream=0) -> int:
+    return LIB.pf8_gemm_bf16(m, n, k, a, lda, b, ldb, d, ldd, hip_stream)
 
 
 def pf8_strerror(status: int) -> str:

@@ -137,6 +137,23 @@ int pf8_block_gemm_f32(int layout, int64_t m, int64_t n, int64_t k, const void* 
   return launch_status(pf8::launch_gemm(args, layout == PF8_WGRAD, true, static_cast<hipStream_t>(hip_stream)));
 }
 
+int pf8_gemm_bf16(int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const void* b, int64_t ldb, void* d,
+                  int64_t ldd, void* hip_stream) {
+  if (a == nullptr || b == nullptr || d == nullptr) return PF8_EINVAL;
+  if (m <= 0 || n <= 0 || k <= 0) return PF8_EINVAL;
+  if (k % kGroup != 0) return PF8_ESHAPE;
+  if (lda < k || ldb < k || ldd < n) return PF8_EINVAL;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(d)) return PF8_EALIGN;
+  if ((lda * 2) % 16 != 0 || (ldb * 2) % 16 != 0 || (ldd * 2) % 16 != 0) return PF8_EALIGN;
+  if (lda * 2 > kMaxTilePitch || ldb * 2 > kMaxTilePitch) return PF8_ESHAPE;
+  if ((m + 127) / 128 * ((n + 127) / 128) > (int64_t{1} << 31) - 1) return PF8_ESHAPE;
+  if (int s = device_status(); s != PF8_OK) return s;
+  // the kernel streams bytes: K and the pitches in bytes, no scales
+  pf8::GemmArgs args{m, n, 2 * k, static_cast<const uint8_t*>(a), 2 * lda, nullptr, 0, static_cast<const uint8_t*>(b),
+                     2 * ldb, nullptr, 0, 0, static_cast<uint16_t*>(d), ldd, nullptr, 0};
+  return launch_status(pf8::launch_gemm_bf16(args, static_cast<hipStream_t>(hip_stream)));
+}
+
 int pf8_block_gemm(int layout, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const float* a_dscale,
                    int64_t ld_as, const void* b, int64_t ldb, const float* b_dscale, int64_t sb_n, int64_t sb_k,
                    void* d, int64_t ldd, void* hip_stream) {

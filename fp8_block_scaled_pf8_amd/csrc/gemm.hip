@@ -34,6 +34,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kBufferFlags = 0x00020000;  // raw buffer resource word 3 for gfx9-family (dword data)
 
@@ -50,6 +51,13 @@ __device__ __forceinline__ v8i lds_read32(const uint8_t* base, int off0, int off
   const v4i lo = *reinterpret_cast<const v4i*>(base + off0);
   const v4i hi = *reinterpret_cast<const v4i*>(base + off1);
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// First (H = 0) or second (H = 1) 16 bytes of a 32-byte operand fragment, as 8 BF16 values.
+template <int H>
+__device__ __forceinline__ bf16x8 bf16_half(v8i v) {
+  const v4i h = H == 0 ? v4i{v[0], v[1], v[2], v[3]} : v4i{v[4], v[5], v[6], v[7]};
+  return __builtin_bit_cast(bf16x8, h);
 }
 
 // Store 4 consecutive BF16 outputs of row m starting at column n (masked at the ragged edges).
@@ -357,7 +365,12 @@ __device__ __forceinline__ void interleave_groups() {
 //    a fixed LDS object and the compiler can track each buffer's direct-to-LDS loads separately.
 //  * The block scales of a stage travel with its operands: they are loaded into the scale registers
 //    of the stage's buffer when the stage is issued, NST stages before use.
-template <int BM, int BN, bool ROW_B, bool EDGE, int NST, bool F32 = false>
+// BF16IN: the operands are BF16 instead of E4M3 codes and carry no scales (the plain BF16 GEMM
+// kept for comparison); K, the pitches and the stage size are then counted in bytes, a 64-byte
+// stage is 32 values, and each fragment pair feeds two v_mfma_f32_32x32x16_bf16 (its first and
+// second 16 bytes hold K values {0..7, 16..23} and {8..15, 24..31} of the stage in both
+// operands, so every product of the stage is formed exactly once).
+template <int BM, int BN, bool ROW_B, bool EDGE, int NST, bool F32 = false, bool BF16IN = false>
 __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, int tiles_n) {
   constexpr int BK = 64;
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
@@ -440,7 +453,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   auto issue_stage = [&](auto u_c, int s) {
     constexpr int u = decltype(u_c)::value;
     uint8_t* buf = bufs(u);
-    load_scales(s, sc_a[u], sc_b[u]);
+    if constexpr (!BF16IN) load_scales(s, sc_a[u], sc_b[u]);
     const int kofs = s * BK;
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
@@ -501,28 +514,38 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
     // decode this stage's scales; the empty asm hands each raw value over opaquely so the decode
     // (and the wait for its load, issued NST stages ago) cannot be hoisted next to the load
     int sae[TM], sbe[TN];
+    if constexpr (!BF16IN) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      uint32_t v = sc_a[u][i];
-      asm volatile("" : "+v"(v));
-      sae[i] = static_cast<int>(v >> 23);
+      for (int i = 0; i < TM; ++i) {
+        uint32_t v = sc_a[u][i];
+        asm volatile("" : "+v"(v));
+        sae[i] = static_cast<int>(v >> 23);
+      }
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        uint32_t v = sc_b[u][j];
+        asm volatile("" : "+v"(v));
+        sbe[j] = static_cast<int>(v >> 23);
+      }
+#pragma unroll
+      for (int j = SB; j < TN; ++j) sbe[j] = sbe[0];
     }
-#pragma unroll
-    for (int j = 0; j < SB; ++j) {
-      uint32_t v = sc_b[u][j];
-      asm volatile("" : "+v"(v));
-      sbe[j] = static_cast<int>(v >> 23);
-    }
-#pragma unroll
-    for (int j = SB; j < TN; ++j) sbe[j] = sbe[0];
     auto mfma_rows = [&](int i0, int i1) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         if (i < i0 || i >= i1) continue;
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0, sbe[j],
-                                                                      0, sae[i]);
+        for (int j = 0; j < TN; ++j) {
+          if constexpr (BF16IN) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16_half<0>(fb[f][j]), bf16_half<0>(fa[f][i]),
+                                                                acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16_half<1>(fb[f][j]), bf16_half<1>(fa[f][i]),
+                                                                acc[i][j], 0, 0, 0);
+          } else {
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0,
+                                                                        sbe[j], 0, sae[i]);
+          }
+        }
       }
     };
     mfma_rows(0, TM / 2);
@@ -555,7 +578,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
     if constexpr (!last) {
       if constexpr (fn != f) {
         // operand reads early in the second half (needed first thing next stage), refill loads late
-        interleave_groups<(TM - TM / 2) * TN, D + TM + SB, 2 * (TM + TN)>();
+        interleave_groups<(TM - TM / 2) * TN * (BF16IN ? 2 : 1), D + (BF16IN ? 0 : TM + SB), 2 * (TM + TN)>();
       } else {
         // with an odd number of buffers the last one hands over to the same fragment set: the
         // remaining operands are read once the MFMAs above have consumed the registers
@@ -770,6 +793,34 @@ static hipError_t launch_tile(const GemmArgs& args, hipStream_t stream) {
 template <int BM, int BN, bool MX>
 static hipError_t launch_tile(const GemmArgs& args, bool row_b, hipStream_t stream) {
   return row_b ? launch_tile<BM, BN, true, MX>(args, stream) : launch_tile<BM, BN, false, MX>(args, stream);
+}
+
+// Plain BF16 GEMM (comparison kernel): the MX pipeline on BF16 operands, 256x256 or 128x128 tiles.
+// args.k, args.lda and args.ldb are in bytes here.
+template <int BM, int BN>
+static hipError_t launch_bf16_tile(const GemmArgs& args, hipStream_t stream) {
+  const int tiles_m = static_cast<int>((args.m + BM - 1) / BM);
+  const int tiles_n = static_cast<int>((args.n + BN - 1) / BN);
+  const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n)), block(256);
+  const bool edge = args.m % BM != 0 || args.n % BN != 0;
+  const int64_t ns = args.k / 64;
+  if (edge) {
+    if (ns >= 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false, true, 5, false, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
+    else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false, true, 2, false, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
+  } else {
+    if (ns >= 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false, false, 5, false, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
+    else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false, false, 2, false, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16(const GemmArgs& args, hipStream_t stream) {
+  const int64_t t256 = ((args.m + 255) / 256) * ((args.n + 255) / 256);
+  const int64_t t128 = ((args.m + 127) / 128) * ((args.n + 127) / 128);
+  // same model as the FP8 tile choice: rounds of one tile per CU x tile area / efficiency
+  const double c256 = static_cast<double>((t256 + 255) / 256) * 65536.0;
+  const double c128 = static_cast<double>((t128 + 255) / 256) * 16384.0 / 0.7;
+  return c256 <= c128 ? launch_bf16_tile<256, 256>(args, stream) : launch_bf16_tile<128, 128>(args, stream);
 }
 
 // Macro-tile choice (MX variant). A launch takes ceil(tiles / 256) rounds of one tile per CU, so

@@ -36,4 +36,7 @@ struct GemmArgs {
 // mx: apply the scales inside the block-scaled MFMA; otherwise promote in FP32 registers.
 hipError_t launch_gemm(const GemmArgs& args, bool row_b_scale, bool mx, hipStream_t stream);
 
+// Plain BF16 GEMM D = A . B^T (no scales); args.k, lda, ldb in bytes, a_dscale / b_dscale unused.
+hipError_t launch_gemm_bf16(const GemmArgs& args, hipStream_t stream);
+
 }  // namespace pf8

@@ -145,6 +145,25 @@ def block_gemm_f32(layout: int, a: torch.Tensor, a_dscale: torch.Tensor, b: torc
     return out
 
 
+def gemm_bf16(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """D[m, n] = sum_k A[m, k] B[n, k] on BF16 operands (the BF16 comparison kernel)."""
+    _check_2d(a, torch.bfloat16, "a")
+    _check_2d(b, torch.bfloat16, "b")
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k:
+        raise ValueError(f"reduction dims differ: a {tuple(a.shape)}, b {tuple(b.shape)}")
+    if out is None:
+        pitch = (n + 7) // 8 * 8
+        out = torch.empty((m, pitch), dtype=torch.bfloat16, device=a.device)[:, :n]
+    _check_2d(out, torch.bfloat16, "out")
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out has the wrong shape")
+    L.check(L.pf8_gemm_bf16(m, n, k, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0), out.data_ptr(),
+                            out.stride(0), _stream(a)), "pf8_gemm_bf16")
+    return out
+
+
 def fprop(qx, sx, qw, sw, out=None, variant: int = L.PF8_GEMM_AUTO) -> torch.Tensor:
     """Y = X . W^T from row-mode X codes and W tile codes."""
     return block_gemm(L.PF8_FPROP, qx, sx, qw, sw, sw.stride(0), 1, out, variant)

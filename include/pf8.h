@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define PF8_ABI_VERSION 3
+#define PF8_ABI_VERSION 4
 
 /* Status codes (int). */
 #define PF8_OK 0
@@ -154,6 +154,20 @@ int pf8_block_gemm_f32(int layout, int64_t m, int64_t n, int64_t k,
                        const void* a, int64_t lda, const float* a_dscale, int64_t ld_as,
                        const void* b, int64_t ldb, const float* b_dscale, int64_t sb_n, int64_t sb_k,
                        float* d, int64_t ldd, int accumulate, void* hip_stream);
+
+/*
+ * Plain BF16 GEMM, the comparison point for the FP8 path [the pages measure FP8 training against
+ * BF16 training of the same model: bit.fan article, "FP8 训练换来 1.36 倍吞吐提升"; paperlayer.ai
+ * summary, appendix C]: the same pipeline and tiles as the FP8 kernels, on BF16 operands.
+ *
+ *   D[i, j] = sum_k A[i, k] * B[j, k]     (FP32 accumulation, BF16 round-to-nearest-even output)
+ *
+ * a: bf16 [m, k], pitch lda >= k; b: bf16 [n, k], pitch ldb >= k (both K-contiguous, as every
+ * operand here); d: bf16 [m, n], pitch ldd >= n. m, n >= 1 (any value), k % 128 == 0.
+ * Bases 16-byte aligned, pitches multiples of 16 bytes; lda, ldb <= (2^31 - 1) / 512.
+ */
+int pf8_gemm_bf16(int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const void* b, int64_t ldb,
+                  void* d, int64_t ldd, void* hip_stream);
 
 /* Static, NUL-terminated description of a status code ("unknown status" for other values). */
 const char* pf8_strerror(int status);

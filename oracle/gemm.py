@@ -97,7 +97,9 @@ def gemm_blockwise_exact(qa, sa_rows, qb, sb_rows) -> list:
 
 
 def unquantized_reference(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
-    """float64 A . B^T of the bf16 inputs, without quantisation (sanity reference)."""
+    """float64 A . B^T of the bf16 inputs, without quantisation: the sanity reference for the
+    quantisation error, and the definition the plain BF16 comparison GEMM is checked against
+    (products of two bf16 values are exact in float64; only the additions round, at 2^-53)."""
     def f64(bits):
         return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return f64(a_bits) @ f64(b_bits).T

@@ -26,7 +26,8 @@ def _declared_functions():
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
     assert names == sorted(["pf8_quant_act_1x128", "pf8_quant_act_dual", "pf8_quant_w_128x128", "pf8_block_gemm",
-                            "pf8_block_gemm_variant", "pf8_block_gemm_f32", "pf8_strerror", "pf8_abi_version"])
+                            "pf8_block_gemm_variant", "pf8_block_gemm_f32", "pf8_gemm_bf16", "pf8_strerror",
+                            "pf8_abi_version"])
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -187,6 +188,25 @@ def test_gemm_f32_validation():
     assert _gf(lda=1 << 24, ldb=1 << 24) == L.PF8_ESHAPE
 
 
+def _gb(**kw):
+    a = dict(m=256, n=384, k=512, a=A16, lda=512, b=B16, ldb=512, d=C16, ldd=384)
+    a.update(kw)
+    return L.pf8_gemm_bf16(a["m"], a["n"], a["k"], a["a"], a["lda"], a["b"], a["ldb"], a["d"], a["ldd"], 0)
+
+
+def test_gemm_bf16_validation():
+    for key in ["a", "b", "d"]:
+        assert _gb(**{key: 0}) == L.PF8_EINVAL, key
+    assert _gb(n=0) == L.PF8_EINVAL
+    assert _gb(k=200, lda=512, ldb=512) == L.PF8_ESHAPE
+    assert _gb(lda=256) == L.PF8_EINVAL
+    assert _gb(ldd=300) == L.PF8_EINVAL
+    assert _gb(a=A16 + 2) == L.PF8_EALIGN
+    assert _gb(lda=516) == L.PF8_EALIGN  # 1032-byte pitch
+    assert _gb(ldd=388) == L.PF8_EALIGN
+    assert _gb(lda=1 << 23, ldb=1 << 23) == L.PF8_ESHAPE
+
+
 def test_no_device_is_reported_after_validation():
     # valid arguments pass validation and then find no device; with a GPU present these fake
     # addresses would reach a kernel, so this runs only where there is none
@@ -200,6 +220,7 @@ def test_no_device_is_reported_after_validation():
     assert _qa() == L.PF8_ENODEV
     assert _qd() == L.PF8_ENODEV
     assert _gf() == L.PF8_ENODEV
+    assert _gb() == L.PF8_ENODEV
     assert _gf(accumulate=0, m=3, n=5, ld_as=3, ldd=8) == L.PF8_ENODEV
     assert _qw() == L.PF8_ENODEV
     assert _gm() == L.PF8_ENODEV

@@ -400,3 +400,46 @@ def test_gemm_f32_validation_on_device():
     assert pf8.pf8_block_gemm_f32(*args, 0, st) == pf8._lib.PF8_OK
     torch.cuda.synchronize()
     assert torch.count_nonzero(d) == 0
+
+
+# ---- plain BF16 GEMM (comparison kernel) against float64 A . B^T ----
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 128), (3, 130, 256), (257, 129, 384), (640, 448, 2048), (2309, 1000, 640),
+                                   (512, 512, 128)])
+def test_gemm_bf16_matches_definition(m, n, k):
+    ab = _rand_bits((m, k), m + k)
+    bb = _rand_bits((n, k), n + 2 * k, 0.02, outliers=False)
+    d = pf8.gemm_bf16(to_dev_bf16(ab), to_dev_bf16(bb))
+    torch.cuda.synchronize()
+    _report(bf16_f64(d), oracle.unquantized_reference(ab, bb), f"bf16 {m}x{n}x{k}")
+
+
+def test_gemm_bf16_small_integers_exact():
+    rng = np.random.default_rng(8)
+    for m, n, k in [(64, 64, 128), (300, 260, 1024)]:
+        a = rng.integers(-4, 5, size=(m, k)).astype(np.float32)
+        b = rng.integers(-4, 5, size=(n, k)).astype(np.float32)
+        ab, bb = f32_to_bf16_bits(a), f32_to_bf16_bits(b)
+        d = pf8.gemm_bf16(to_dev_bf16(ab), to_dev_bf16(bb))
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(d), oracle.bf16_round_from_f64(oracle.unquantized_reference(ab, bb)))
+
+
+def test_gemm_bf16_padded_pitches():
+    m, n, k = 300, 200, 384
+    ab = _rand_bits((m, k), 91)
+    bb = _rand_bits((n, k), 92, 0.02, outliers=False)
+    abig = np.zeros((m, k + 64), np.uint16)
+    abig[:, :k] = ab
+    bbig = np.zeros((n, k + 128), np.uint16)
+    bbig[:, :k] = bb
+    canary = 0x7F80
+    d = torch.full((m, 208), 0, dtype=torch.int16, device=DEV).fill_(canary).view(torch.bfloat16)
+    a_d, b_d = to_dev_bf16(abig), to_dev_bf16(bbig)
+    pf8._lib.check(pf8.pf8_gemm_bf16(m, n, k, a_d.data_ptr(), k + 64, b_d.data_ptr(), k + 128, d.data_ptr(), 208,
+                                     torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    bits = bf16_bits(d)
+    assert np.all(bits[:, n:] == canary)
+    _report((bits[:, :n].astype(np.uint32) << 16).view(np.float32).astype(np.float64),
+            oracle.unquantized_reference(ab, bb), "bf16 padded")

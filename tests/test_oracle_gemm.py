@@ -210,3 +210,22 @@ def test_workload_generator_recipe():
     a = generate("mlp_gateup_fprop", only=["X"])["X"]
     b = generate("mlp_gateup_layer_step", only=["X"])["X"]
     assert np.array_equal(a, b)
+
+
+def test_unquantized_reference_brute_force_and_closed_forms():
+    """The plain BF16 product A . B^T: small integers against an integer triple loop, identity and
+    a hand-computed 2x2 example."""
+    rng = np.random.default_rng(17)
+    a = rng.integers(-8, 9, size=(5, 7)).astype(np.float32)
+    b = rng.integers(-8, 9, size=(3, 7)).astype(np.float32)
+    got = unquantized_reference(f32_to_bf16_bits(a), f32_to_bf16_bits(b))
+    want = [[sum(int(a[i, k]) * int(b[j, k]) for k in range(7)) for j in range(3)] for i in range(5)]
+    assert np.array_equal(got, np.array(want, dtype=np.float64))
+    x = rng.standard_normal((4, 6)).astype(np.float32)
+    xb = f32_to_bf16_bits(x)
+    eye = f32_to_bf16_bits(np.eye(6, dtype=np.float32))
+    assert np.array_equal(unquantized_reference(xb, eye), (xb.astype(np.uint32) << 16).view(np.float32))
+    # [1.5, -2] . [[0.25, 4], [3, 0.5]]^T = [1.5*0.25 - 8, 4.5 - 1] = [-7.625, 3.5]
+    two = unquantized_reference(f32_to_bf16_bits(np.array([[1.5, -2.0]], np.float32)),
+                                f32_to_bf16_bits(np.array([[0.25, 4.0], [3.0, 0.5]], np.float32)))
+    assert two.tolist() == [[-7.625, 3.5]]
