@@ -327,16 +327,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p, int tiles_m, int 
   }
 }
 
-// Scheduling pattern for NM MFMAs: the ND LDS reads go out spread over the first half of the
-// MFMAs (their data is needed at the start of the next stage), the NV vector-memory reads (refill
-// loads, needed only stages later) over the second half (sched_group_barrier masks: 0x008 MFMA,
-// 0x020 VMEM read, 0x100 DS read).
+// Scheduling pattern for NM MFMAs: the ND LDS reads and the NV vector-memory reads go out spread
+// evenly between them (sched_group_barrier masks: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read).
+// Bunching the refill loads behind the last few MFMAs fills the texture unit's queues and stalls
+// the wave's instruction stream, matrix instructions included.
 template <int NM, int NV, int ND, int X = 0>
 __device__ __forceinline__ void interleave_groups() {
   if constexpr (X < NM) {
-    constexpr int H = NM / 2;
-    constexpr int d = X < H ? (ND * (X + 1)) / H - (ND * X) / H : 0;
-    constexpr int v = X >= H ? (NV * (X - H + 1)) / (NM - H) - (NV * (X - H)) / (NM - H) : 0;
+    constexpr int d = (ND * (X + 1)) / NM - (ND * X) / NM;
+    constexpr int v = (NV * (X + 1)) / NM - (NV * X) / NM;
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);
     if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
@@ -438,9 +437,14 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   // with tile scales and a wave's columns inside one 128-column tile, one B scale serves all j
   constexpr bool B_ONE = !ROW_B && (WN == 128) && !EDGE;
   constexpr int SB = B_ONE ? 1 : TN;
+  // vector-memory operations a wave issues per stage: scale loads and direct-to-LDS loads
+  constexpr int VV = D + (BF16IN ? 0 : TM + SB);
   uint32_t sc_a[NBUF][TM], sc_b[NBUF][SB];
   auto load_scales = [&](int s, uint32_t (&sa)[TM], uint32_t (&sb)[SB]) {
-    const int64_t kb = s >> 1;
+    int64_t kb = s >> 1;
+    // the two stages of a K block load the same scales; an opaque block index keeps the second
+    // set of loads from being merged into the first, so every stage issues exactly VV operations
+    asm volatile("" : "+s"(kb));
 #pragma unroll
     for (int i = 0; i < TM; ++i) sa[i] = __float_as_uint(p.a_dscale[kb * p.ld_as + a_row[i]]);
 #pragma unroll
@@ -503,8 +507,14 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // s_waitcnt: vmcnt(n) with lgkmcnt(0) (and no expcnt wait)
-#define PF8_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0x0 << 8))
+  // s_waitcnt vmcnt(n) lgkmcnt(0) (no expcnt wait). Vector memory operations complete in issue
+  // order, so vmcnt(n) with n = the operations issued after a stage's last load guarantees that
+  // stage. n is capped at the counter's 63, which only waits longer.
+#define PF8_WAIT_VM_LGKM0(n0)                                                                  \
+  do {                                                                                         \
+    constexpr int n_ = (n0) < 63 ? (n0) : 63;                                                  \
+    __builtin_amdgcn_s_waitcnt((n_ & 0xF) | ((n_ >> 4) << 14) | (0x7 << 4) | (0x0 << 8));      \
+  } while (0)
 
   // one stage: s = stage index, u = its buffer (compile-time), refill = issue stage s + NST into u
   auto stage = [&](int s, auto u_c, bool refill, auto last_c) {
@@ -553,19 +563,19 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
     // busy while the waves line up
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (!last) {
-      // stages s+2 .. s+NST-1 may still be in flight (fewer near the end of K)
+      // stages s+2 .. s+NST-1 (VV operations each) may still be in flight (fewer near the end of K)
       if (refill) {
-        PF8_WAIT_VM_LGKM0(D * (NST - 2));
+        PF8_WAIT_VM_LGKM0(VV * (NST - 2));
       } else {
         const int after = ns - 2 - s;  // stages issued after stage s+1
         if constexpr (NST >= 5) {
-          if (after >= 3) PF8_WAIT_VM_LGKM0(D * 3);
-          else if (after == 2) PF8_WAIT_VM_LGKM0(D * 2);
-          else if (after == 1) PF8_WAIT_VM_LGKM0(D);
+          if (after >= 3) PF8_WAIT_VM_LGKM0(VV * 3);
+          else if (after == 2) PF8_WAIT_VM_LGKM0(VV * 2);
+          else if (after == 1) PF8_WAIT_VM_LGKM0(VV);
           else PF8_WAIT_VM_LGKM0(0);
         } else {
-          if (after >= 2) PF8_WAIT_VM_LGKM0(D * 2);
-          else if (after == 1) PF8_WAIT_VM_LGKM0(D);
+          if (after >= 2) PF8_WAIT_VM_LGKM0(VV * 2);
+          else if (after == 1) PF8_WAIT_VM_LGKM0(VV);
           else PF8_WAIT_VM_LGKM0(0);
         }
       }
@@ -610,7 +620,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
       issue_stage(std::integral_constant<int, (3 - H + NST) % NST>{}, 3);
     }
     if constexpr (NST >= 5) issue_stage(std::integral_constant<int, (4 - H + NST) % NST>{}, 4);
-    PF8_WAIT_VM_LGKM0(D * (NST - 1));
+    PF8_WAIT_VM_LGKM0(VV * (NST - 1));
     __builtin_amdgcn_s_barrier();
     constexpr int u0 = (NST - H) % NST;
     read_frags(bufs(u0), fa[u0 & 1], fb[u0 & 1]);
