@@ -356,8 +356,10 @@ __device__ __forceinline__ void interleave_groups() {
 //    banks; with this swizzle those 16 chunks land in 16 distinct 4-bank groups.
 //  * Per stage and wave: TM*TN MFMAs split in two halves; between them the wave waits until its own
 //    loads of the next stage have landed and its operand reads are done (explicit s_waitcnt), meets
-//    the others at s_barrier, refills the buffer all waves have just finished reading, and reads the
-//    next stage's operands into the other fragment set while the second half of the MFMAs runs.
+//    the others at s_barrier, starts refilling the buffer all waves have just finished reading, and
+//    reads the next stage's operands into the other fragment set while the second half of the
+//    MFMAs runs. The refill's A-operand loads go out in that second half, its scales and B-operand
+//    loads in the first half of the next stage, so the texture unit sees a steady stream.
 //  * Stage s lives in buffer (s - h) mod NST with h = (stage count) mod NST, so that the main loop
 //    (unrolled by NST) and the final NST stages always use buffers 0..NST-1 in order; only the first
 //    h stages (a short head, one code path per h) start elsewhere. Every buffer access thereby names
@@ -454,26 +456,35 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
     }
   };
 
-  auto issue_stage = [&](auto u_c, int s) {
+  // Loads of stage s into buffer u: part 0 = the A operand's direct-to-LDS loads, part 1 = the
+  // stage's scales and the B operand's loads, part 2 = all of them.
+  auto issue_part = [&](auto u_c, int s, auto part_c) {
+    constexpr int part = decltype(part_c)::value;
     constexpr int u = decltype(u_c)::value;
     uint8_t* buf = bufs(u);
-    if constexpr (!BF16IN) load_scales(s, sc_a[u], sc_b[u]);
+    if constexpr (!BF16IN && part != 0) load_scales(s, sc_a[u], sc_b[u]);
     const int kofs = s * BK;
 #pragma unroll
-    for (int j = 0; j < A_DMA; ++j) {
+    for (int j = 0; j < (part == 1 ? 0 : A_DMA); ++j) {
       const int slab = wave + 4 * j;  // rows 16*slab .. +15 of the A tile
       auto* dst = (__attribute__((address_space(3))) void*)(buf + slab * 16 * BK);
       if (EDGE) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, dst, 16, voff_a + slab * 16 * lda, kofs, 0, 0);
       else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, dst, 16, voff_a, slab * 16 * lda + kofs, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < B_DMA; ++j) {
+    for (int j = 0; j < (part == 0 ? 0 : B_DMA); ++j) {
       const int slab = wave + 4 * j;
       auto* dst = (__attribute__((address_space(3))) void*)(buf + A_ST + slab * 16 * BK);
       if (EDGE) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, dst, 16, voff_b + slab * 16 * ldb, kofs, 0, 0);
       else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, dst, 16, voff_b, slab * 16 * ldb + kofs, 0, 0);
     }
   };
+  using PA = std::integral_constant<int, 0>;
+  using PB = std::integral_constant<int, 1>;
+  using PALL = std::integral_constant<int, 2>;
+  auto issue_stage = [&](auto u_c, int s) { issue_part(u_c, s, PALL{}); };
+  // vector-memory operations of the two parts of a refill
+  constexpr int VA = A_DMA, VB = VV - A_DMA;
 
   // ---- operand fragments: set f = (buffer index) & 1 ----
   const int sw = (l32 >> 2) & 3;
@@ -516,9 +527,13 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
     __builtin_amdgcn_s_waitcnt((n_ & 0xF) | ((n_ >> 4) << 14) | (0x7 << 4) | (0x0 << 8));      \
   } while (0)
 
-  // one stage: s = stage index, u = its buffer (compile-time), refill = issue stage s + NST into u
-  auto stage = [&](int s, auto u_c, bool refill, auto last_c) {
+  // One stage: s = stage index, u = its buffer (compile-time). A refill of buffer u with stage
+  // s + NST is split in two to spread the loads over a whole stage of MFMAs: with `refill` the
+  // A-operand loads go out in this stage's second half; with `prev` this stage's first half sends
+  // the scales and B-operand loads of the previous stage's refill (stage s - 1 + NST).
+  auto stage = [&](int s, auto u_c, bool refill, auto last_c, auto prev_c) {
     constexpr int u = decltype(u_c)::value;
+    constexpr bool prev = decltype(prev_c)::value;
     constexpr bool last = decltype(last_c)::value;
     constexpr int f = u & 1, un = (u + 1) % NST, fn = un & 1;
     // decode this stage's scales; the empty asm hands each raw value over opaquely so the decode
@@ -558,7 +573,10 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
         }
       }
     };
+    // second part of the previous stage's refill (its buffer is free since the last barrier)
+    if constexpr (prev) issue_part(std::integral_constant<int, (u + NST - 1) % NST>{}, s - 1 + NST, PB{});
     mfma_rows(0, TM / 2);
+    if constexpr (prev) interleave_groups<(TM / 2) * TN * (BF16IN ? 2 : 1), VB, 0>();  // loads between the MFMAs
     // the first half of the MFMAs stays ahead of the wait and barrier: it keeps the matrix core
     // busy while the waves line up
     __builtin_amdgcn_sched_barrier(0);
@@ -580,15 +598,15 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
         }
       }
       __builtin_amdgcn_s_barrier();
-      if (refill) issue_stage(u_c, s + NST);
+      if (refill) issue_part(u_c, s + NST, PA{});
       if constexpr (fn != f) read_frags(bufs(un), fa[fn], fb[fn]);
       else read_frags_a(bufs(un), fa[fn], 0, TM / 2);  // only A rows the first half no longer needs
     }
     mfma_rows(TM / 2, TM);
     if constexpr (!last) {
       if constexpr (fn != f) {
-        // operand reads early in the second half (needed first thing next stage), refill loads late
-        interleave_groups<(TM - TM / 2) * TN * (BF16IN ? 2 : 1), D + (BF16IN ? 0 : TM + SB), 2 * (TM + TN)>();
+        // next-stage operand reads and the refill's A-operand loads between the MFMAs
+        interleave_groups<(TM - TM / 2) * TN * (BF16IN ? 2 : 1), VA, 2 * (TM + TN)>();
       } else {
         // with an odd number of buffers the last one hands over to the same fragment set: the
         // remaining operands are read once the MFMAs above have consumed the registers
@@ -612,23 +630,26 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   const int h = ns % NST;
   auto prologue = [&](auto h_c) {
     constexpr int H = decltype(h_c)::value;
-    // stages 0 .. NST-1, issued in stage order (the explicit waits count loads in that order)
+    // stages 0 .. NST-1, issued in stage order (the explicit waits count loads in that order); of
+    // stage NST-1 only the A-operand part, stage 0 sends the rest like any refill's second part
     issue_stage(std::integral_constant<int, (0 - H + NST) % NST>{}, 0);
-    issue_stage(std::integral_constant<int, (1 - H + NST) % NST>{}, 1);
+    if constexpr (NST == 2) issue_part(std::integral_constant<int, (1 - H + NST) % NST>{}, 1, PA{});
+    else issue_stage(std::integral_constant<int, (1 - H + NST) % NST>{}, 1);
     if constexpr (NST >= 4) {
       issue_stage(std::integral_constant<int, (2 - H + NST) % NST>{}, 2);
-      issue_stage(std::integral_constant<int, (3 - H + NST) % NST>{}, 3);
+      if constexpr (NST == 4) issue_part(std::integral_constant<int, (3 - H + NST) % NST>{}, 3, PA{});
+      else issue_stage(std::integral_constant<int, (3 - H + NST) % NST>{}, 3);
     }
-    if constexpr (NST >= 5) issue_stage(std::integral_constant<int, (4 - H + NST) % NST>{}, 4);
-    PF8_WAIT_VM_LGKM0(VV * (NST - 1));
+    if constexpr (NST >= 5) issue_part(std::integral_constant<int, (4 - H + NST) % NST>{}, 4, PA{});
+    PF8_WAIT_VM_LGKM0(VV * (NST - 2) + VA);
     __builtin_amdgcn_s_barrier();
     constexpr int u0 = (NST - H) % NST;
     read_frags(bufs(u0), fa[u0 & 1], fb[u0 & 1]);
     // head stages 0 .. H-1 in buffers NST-H .. NST-1 (all refill: ns >= NST + H)
-    if constexpr (H >= 1) stage(0, std::integral_constant<int, NST - H>{}, true, F{});
-    if constexpr (H >= 2) stage(1, std::integral_constant<int, NST - H + 1>{}, true, F{});
-    if constexpr (H >= 3) stage(2, std::integral_constant<int, NST - H + 2>{}, true, F{});
-    if constexpr (H >= 4) stage(3, std::integral_constant<int, NST - H + 3>{}, true, F{});
+    if constexpr (H >= 1) stage(0, std::integral_constant<int, NST - H>{}, true, F{}, T{});
+    if constexpr (H >= 2) stage(1, std::integral_constant<int, NST - H + 1>{}, true, F{}, T{});
+    if constexpr (H >= 3) stage(2, std::integral_constant<int, NST - H + 2>{}, true, F{}, T{});
+    if constexpr (H >= 4) stage(3, std::integral_constant<int, NST - H + 3>{}, true, F{}, T{});
   };
   if constexpr (NST == 5) {
     switch (h) {
@@ -653,29 +674,29 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   // ---- main loop: NST stages per trip, buffers 0 .. NST-1 ----
   int s = h;
   for (; s < ns - NST; s += NST) {
-    stage(s, I0{}, true, F{});
-    stage(s + 1, I1{}, true, F{});
+    stage(s, I0{}, true, F{}, T{});
+    stage(s + 1, I1{}, true, F{}, T{});
     if constexpr (NST >= 4) {
-      stage(s + 2, I2{}, true, F{});
-      stage(s + 3, I3{}, true, F{});
+      stage(s + 2, I2{}, true, F{}, T{});
+      stage(s + 3, I3{}, true, F{}, T{});
     }
-    if constexpr (NST >= 5) stage(s + 4, I4{}, true, F{});
+    if constexpr (NST >= 5) stage(s + 4, I4{}, true, F{}, T{});
   }
   // ---- last NST stages: nothing left to fetch ----
   if constexpr (NST == 5) {
-    stage(s, I0{}, false, F{});
-    stage(s + 1, I1{}, false, F{});
-    stage(s + 2, I2{}, false, F{});
-    stage(s + 3, I3{}, false, F{});
-    stage(s + 4, I4{}, false, T{});
+    stage(s, I0{}, false, F{}, T{});
+    stage(s + 1, I1{}, false, F{}, F{});
+    stage(s + 2, I2{}, false, F{}, F{});
+    stage(s + 3, I3{}, false, F{}, F{});
+    stage(s + 4, I4{}, false, T{}, F{});
   } else if constexpr (NST == 4) {
-    stage(s, I0{}, false, F{});
-    stage(s + 1, I1{}, false, F{});
-    stage(s + 2, I2{}, false, F{});
-    stage(s + 3, I3{}, false, T{});
+    stage(s, I0{}, false, F{}, T{});
+    stage(s + 1, I1{}, false, F{}, F{});
+    stage(s + 2, I2{}, false, F{}, F{});
+    stage(s + 3, I3{}, false, T{}, F{});
   } else {
-    stage(s, I0{}, false, F{});
-    stage(s + 1, I1{}, false, T{});
+    stage(s, I0{}, false, F{}, T{});
+    stage(s + 1, I1{}, false, T{}, F{});
   }
 #undef PF8_WAIT_VM_LGKM0
 
