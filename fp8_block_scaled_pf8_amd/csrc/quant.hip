@@ -5,9 +5,10 @@
 // 128 values along the reduction dimension for activations/gradients, per 128x128 tile for
 // weights, each computed from its own block when the tensor is quantised.
 //
-// All three kernels are HBM-bound streams (2 B read + ~1 B written per element): one read of the
-// input, block maxima reduced in registers / across lanes, then exact power-of-two scaling and
-// the hardware fp32 -> E4M3 RNE conversion.
+// All kernels are HBM-bound streams (2 B read + ~1 B written per element and grouping): one read
+// of the input, block maxima reduced in registers / across lanes, then gfx950's scaled conversion
+// (v_cvt_scalef32_pk_fp8_bf16: two bf16 divided by the power-of-two scale and rounded to E4M3,
+// nearest even, in one instruction) straight from the bf16 words.
 #include "pf8_device.h"
 #include "pf8_launch.h"
 
@@ -34,16 +35,22 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
     v[u] = make_uint4(0, 0, 0, 0);
     if (r < rows) v[u] = *reinterpret_cast<const uint4*>(x + r * ldx + g * kGroup + lane16 * 8);
   }
+  static_assert(kRowUnroll % 2 == 0, "rows are reduced in pairs");
 #pragma unroll
-  for (int u = 0; u < kRowUnroll; ++u) {
-    const int64_t r = r0 + 16 * u;
-    // every lane of the 16-lane row takes part in the reduction (rows past the end hold zeros)
-    const uint32_t amax = row16_max(amax8_bits(v[u]));
-    const int e = block_exponent(amax);
-    const uint2 codes = quant8(v[u], pow2f(-e));
-    if (r < rows) {
-      *reinterpret_cast<uint2*>(q + r * ldq + g * kGroup + lane16 * 8) = codes;
-      if (lane16 == 0) dscale[g * ld_s + r] = pow2f(e);
+  for (int k = 0; k < kRowUnroll / 2; ++k) {
+    // every lane of the 16-lane row takes part in the reduction (rows past the end hold zeros);
+    // two rows' maxima travel through the DPP reduction packed in one register
+    const uint32_t amax2 = row16_max_pk(pair_amax(amax8_pk(v[2 * k]), amax8_pk(v[2 * k + 1])));
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int u = 2 * k + hh;
+      const int64_t r = r0 + 16 * u;
+      const float scale = pow2f(block_exponent(hh ? amax2 >> 16 : amax2 & 0xFFFFu));
+      const uint2 codes = quant8_scaled(v[u], scale);
+      if (r < rows) {
+        *reinterpret_cast<uint2*>(q + r * ldq + g * kGroup + lane16 * 8) = codes;
+        if (lane16 == 0) dscale[g * ld_s + r] = scale;
+      }
     }
   }
 }
@@ -103,28 +110,27 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
     for (int j = 0; j < 8; ++j) red[wave][8 * cc + j] = m[j];
   }
   __syncthreads();
-  float inv[8];
+  float scale[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int c = 8 * cc + j;
     const uint32_t a = max(max(red[0][c], red[1][c]), max(red[2][c], red[3][c]));
-    const int e = block_exponent(a);
-    inv[j] = pow2f(-e);
-    if (rq == 0 && col_ok) dscale[g * ld_s + c0 + c] = pow2f(e);
+    scale[j] = pow2f(block_exponent(a));
+    if (rq == 0 && col_ok) dscale[g * ld_s + c0 + c] = scale[j];
   }
-  // quantise: for column j, the 4 codes of rows 4rq..4rq+3 form one little-endian dword
+  // quantise: for column j, the 4 codes of rows 4rq..4rq+3 form one little-endian dword; the
+  // column's values of two rows are paired into one dword (v_perm) and converted together
   uint32_t colword[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) colword[j] = 0;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t w[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int pair = cvt2_e4m3<false>(bf16_lo(w[h]) * inv[2 * h], bf16_hi(w[h]) * inv[2 * h + 1], 0);
-      colword[2 * h] |= (static_cast<uint32_t>(pair) & 0xFFu) << (8 * p);
-      colword[2 * h + 1] |= ((static_cast<uint32_t>(pair) >> 8) & 0xFFu) << (8 * p);
-    }
+  for (int j = 0; j < 8; ++j) {
+    const int h = j >> 1;
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;  // high or low bf16 of each row's word
+    const uint32_t w0 = h == 0 ? v[0].x : h == 1 ? v[0].y : h == 2 ? v[0].z : v[0].w;
+    const uint32_t w1 = h == 0 ? v[1].x : h == 1 ? v[1].y : h == 2 ? v[1].z : v[1].w;
+    const uint32_t w2 = h == 0 ? v[2].x : h == 1 ? v[2].y : h == 2 ? v[2].z : v[2].w;
+    const uint32_t w3 = h == 0 ? v[3].x : h == 1 ? v[3].y : h == 2 ? v[3].z : v[3].w;
+    const uint32_t p01 = __builtin_amdgcn_perm(w1, w0, sel), p23 = __builtin_amdgcn_perm(w3, w2, sel);
+    colword[j] = cvt2_bf16_scaled<true>(p23, scale[j], cvt2_bf16_scaled<false>(p01, scale[j], 0u));
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -171,13 +177,12 @@ __global__ __launch_bounds__(256) void quant_w_kernel(const uint16_t* __restrict
   if ((t & 63) == 0) red[t >> 6] = a;
   __syncthreads();
   a = max(max(red[0], red[1]), max(red[2], red[3]));
-  const int e = block_exponent(a);
-  const float inv = pow2f(-e);
-  if (t == 0) dscale[tn * ld_s + tk] = pow2f(e);
+  const float scale = pow2f(block_exponent(a));
+  if (t == 0) dscale[tn * ld_s + tk] = scale;
   uint2 codes[8];
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    codes[p] = quant8(v[p], inv);
+    codes[p] = quant8_scaled(v[p], scale);
     *reinterpret_cast<uint2*>(q + (row0 + p) * ldq + col0) = codes[p];
   }
   if (qt == nullptr) return;  // uniform over the workgroup
@@ -218,13 +223,6 @@ __global__ __launch_bounds__(256) void quant_w_kernel(const uint16_t* __restrict
 // LDS tile: rows c, c+1 (c even) share 256 bytes = all 64 banks; 8-byte slot s of row c sits at
 // slot (s | (c & 1) << 4) ^ (((c >> 3) & 7) << 2) of the pair, so a 16-lane read of two rows'
 // 16-byte chunks touches every bank once.
-typedef unsigned short ushort2_v __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
-  const ushort2_v r = __builtin_elementwise_max(__builtin_bit_cast(ushort2_v, a), __builtin_bit_cast(ushort2_v, b));
-  return __builtin_bit_cast(uint32_t, r);
-}
-
 __device__ __forceinline__ int dual_slot(int c, int s) {
   return (c >> 1) * 256 + 8 * ((s | ((c & 1) << 4)) ^ (((c >> 3) & 7) << 2));
 }
@@ -247,12 +245,18 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
   for (int p = 0; p < 8; ++p) v[p] = *reinterpret_cast<const uint4*>(x + (r0 + 8 * rb + p) * ldx + c0 + 8 * cc);
 
   // ---- row mode: 8 rows, one 128-value group each ----
+  // (row maxima two at a time: packed 16-bit pairs through the DPP reduction)
   float my_row_scale = 0.0f;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int e = block_exponent(row16_max(amax8_bits(v[p])));
-    *reinterpret_cast<uint2*>(qr + (r0 + 8 * rb + p) * ldqr + c0 + 8 * cc) = quant8(v[p], pow2f(-e));
-    if (cc == p) my_row_scale = pow2f(e);
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t rm = row16_max_pk(pair_amax(amax8_pk(v[2 * k]), amax8_pk(v[2 * k + 1])));
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int p = 2 * k + hh;
+      const float scale = pow2f(block_exponent(hh ? rm >> 16 : rm & 0xFFFFu));
+      *reinterpret_cast<uint2*>(qr + (r0 + 8 * rb + p) * ldqr + c0 + 8 * cc) = quant8_scaled(v[p], scale);
+      if (cc == p) my_row_scale = scale;
+    }
   }
   if (cc < 8) sr[gc * ld_sr + r0 + 8 * rb + cc] = my_row_scale;
 
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
   }
   if ((t & 63) < 16) *reinterpret_cast<uint4*>(&red[wave][cc][0]) = make_uint4(m[0], m[1], m[2], m[3]);
   __syncthreads();
-  float inv[8];
+  float scale[8];
   {
     uint4 a = *reinterpret_cast<const uint4*>(&red[0][cc][0]);
 #pragma unroll
@@ -285,29 +289,26 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
     float my_col_scale = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int e = block_exponent((aw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-      inv[j] = pow2f(-e);
-      if (rb == j) my_col_scale = pow2f(e);
+      scale[j] = pow2f(block_exponent((aw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu));
+      if (rb == j) my_col_scale = scale[j];
     }
     // thread (rb < 8, cc) writes the scale of column 8*cc + rb
     if (rb < 8) sc[gr * ld_sc + c0 + 8 * cc + rb] = my_col_scale;
   }
-  // codes of column j for rows 8*rb .. 8*rb+7: one little-endian 64-bit word
+  // codes of column j for rows 8*rb .. 8*rb+7: one little-endian 64-bit word; the column's
+  // values of rows p, p+1 are paired into one dword (v_perm) and converted together
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int h = j >> 1;
-    float f[8];
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;  // high or low bf16 of each row's word
+    uint32_t w[8];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const uint32_t w = h == 0 ? v[p].x : h == 1 ? v[p].y : h == 2 ? v[p].z : v[p].w;
-      f[p] = ((j & 1) ? bf16_hi(w) : bf16_lo(w)) * inv[j];
-    }
-    int lo = cvt2_e4m3<false>(f[0], f[1], 0);
-    lo = cvt2_e4m3<true>(f[2], f[3], lo);
-    int hi = cvt2_e4m3<false>(f[4], f[5], 0);
-    hi = cvt2_e4m3<true>(f[6], f[7], hi);
-    *reinterpret_cast<uint2*>(tile + dual_slot(8 * cc + j, rb)) =
-        make_uint2(static_cast<uint32_t>(lo), static_cast<uint32_t>(hi));
+    for (int p = 0; p < 8; ++p) w[p] = h == 0 ? v[p].x : h == 1 ? v[p].y : h == 2 ? v[p].z : v[p].w;
+    const uint32_t lo = cvt2_bf16_scaled<true>(__builtin_amdgcn_perm(w[3], w[2], sel), scale[j],
+                                               cvt2_bf16_scaled<false>(__builtin_amdgcn_perm(w[1], w[0], sel), scale[j], 0u));
+    const uint32_t hi = cvt2_bf16_scaled<true>(__builtin_amdgcn_perm(w[7], w[6], sel), scale[j],
+                                               cvt2_bf16_scaled<false>(__builtin_amdgcn_perm(w[5], w[4], sel), scale[j], 0u));
+    *reinterpret_cast<uint2*>(tile + dual_slot(8 * cc + j, rb)) = make_uint2(lo, hi);
   }
   __syncthreads();
   // 128 transposed rows of 128 bytes: thread t sends chunk (t & 7) of rows (t >> 3) + 32 * i
