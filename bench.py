@@ -2,9 +2,9 @@
 
 A step is one linear layer's full FP8 pass at the fused MLP gate+up shape of a ~2B decoder
 (X [8192, 2048] bf16 = 2 x 4096 tokens, W [12288, 2048], dY [8192, 12288]):
-  quantise X along K and along the tokens (one read), quantise W by 128x128 tiles (+ transposed
-  codes), fprop Y = X W^T, quantise dY along N and along the tokens (one read), dgrad dX = dY W,
-  wgrad dW = dY^T X.  (--unfused: one quantiser pass per orientation, eight launches.)
+  quantise X along K and along the tokens (one read) and W by 128x128 tiles (+ transposed codes)
+  in one launch, fprop Y = X W^T, quantise dY along N and along the tokens (one read), dgrad
+  dX = dY W, wgrad dW = dY^T X.  (--unfused: one quantiser pass per orientation, eight launches.)
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 
 Printed (one JSON line): value = the three GEMMs' 2*M*N*K flops per step / step GPU time
@@ -34,7 +34,7 @@ PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (AMD published figure, no spar
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "mlp_gateup_layer_step"
 # launch order of one step (LinearStep.launches)
-KERNELS_FUSED = ["quant_x_dual", "quant_w_tiles", "fprop_gemm", "quant_dy_dual", "dgrad_gemm", "wgrad_gemm"]
+KERNELS_FUSED = ["quant_x_dual_w_tiles", "fprop_gemm", "quant_dy_dual", "dgrad_gemm", "wgrad_gemm"]
 KERNELS_UNFUSED = ["quant_x_rows", "quant_w_tiles", "fprop_gemm", "quant_dy_rows", "dgrad_gemm", "quant_dy_cols",
                    "quant_x_cols", "wgrad_gemm"]
 
@@ -72,6 +72,8 @@ def _alg_bytes(name, m, n, k):
         return m * n * 2 + m * n + (m * n // g) * 4
     if name == "quant_x_dual":  # one read, both code sets and scale sets written
         return m * k * 2 + 2 * (m * k + (m * k // g) * 4)
+    if name == "quant_x_dual_w_tiles":
+        return _alg_bytes("quant_x_dual", m, n, k) + _alg_bytes("quant_w_tiles", m, n, k)
     if name == "quant_dy_dual":
         return m * n * 2 + 2 * (m * n + (m * n // g) * 4)
     if name == "quant_w_tiles":
@@ -288,7 +290,7 @@ def summarize_prof(dirs):
             rows = sorted(csv.DictReader(open(f)), key=lambda r: int(r["Start_Timestamp"]))
             pf8_rows = [r for r in rows if "pf8::" in r["Kernel_Name"]]
             seq = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in pf8_rows]
-            dual = any("quant_dual" in r["Kernel_Name"] for r in pf8_rows)
+            dual = any("quant_fwd" in r["Kernel_Name"] for r in pf8_rows)
             kernels = KERNELS_FUSED if dual else KERNELS_UNFUSED
             nsteps = len(seq) // len(kernels)
             if nsteps >= 3 and len(seq) % len(kernels) == 0:
@@ -365,6 +367,20 @@ def main():
             gbs = _alg_bytes(name, m, n, k) / (ms * 1e-3) / 1e9
             entry.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
         kernels[name] = entry
+    # the FP32 weight gradient accumulated into a main gradient (pf8_block_gemm_f32, accumulate=1), on
+    # the step's own codes, timed the same way: reported beside the step, not part of it
+    main_grad = torch.zeros((n, k), dtype=torch.float32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    for _ in range(3):
+        pf8.wgrad_f32(step.qdyt, step.sdyt, step.qxt, step.sxt, out=main_grad, accumulate=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(20):
+        pf8.wgrad_f32(step.qdyt, step.sdyt, step.qxt, step.sxt, out=main_grad, accumulate=True)
+    e1.record(st)
+    torch.cuda.synchronize()
+    f32_us = e0.elapsed_time(e1) * 1e3 / 20
+    del main_grad
     fp_ms = per["fprop_gemm"]
     achieved = 2.0 * m * n * k / (fp_ms * 1e-3) / 1e12
     traffic = measured_traffic() if args.variant == "auto" else None
@@ -384,6 +400,8 @@ def main():
         "wall_ms_per_step": round(ms_step_wall, 4),
         "roofline": roofline,
         "kernels": kernels,
+        "wgrad_f32_accumulate": {"us": round(f32_us, 2), "tflops": round(2.0 * m * n * k / (f32_us * 1e-6) / 1e12, 1),
+                                 "note": "dW in FP32 added to a main gradient (not part of the step)"},
     }
     del step, x, w, dy
     torch.cuda.empty_cache()

@@ -23,7 +23,7 @@ PF8_OK, PF8_EINVAL, PF8_ESHAPE, PF8_EALIGN, PF8_ENODEV, PF8_ELAUNCH = range(6)
 PF8_ALONG_COLS, PF8_ALONG_ROWS = 0, 1
 PF8_FPROP, PF8_DGRAD, PF8_WGRAD = 0, 1, 2
 PF8_GEMM_AUTO, PF8_GEMM_MX_SCALED, PF8_GEMM_PROMOTE = 0, 1, 2
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
@@ -33,6 +33,8 @@ _vp = ctypes.c_void_p
 SIGNATURES = {
     "pf8_quant_act_1x128": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp]),
     "pf8_quant_act_dual": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
+    "pf8_quant_fwd": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp,
+                             _i64, _vp, _i64, _vp, _i64, _vp]),
     "pf8_quant_w_128x128": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
     "pf8_block_gemm": (_int, [_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
     "pf8_block_gemm_variant": (
@@ -71,6 +73,12 @@ def pf8_quant_act_dual(x, rows, cols, ldx, q_row, ldq_row, dscale_row, ld_sr, q_
                        hip_stream=0) -> int:
     return LIB.pf8_quant_act_dual(x, rows, cols, ldx, q_row, ldq_row, dscale_row, ld_sr, q_col, ldq_col, dscale_col,
                                   ld_sc, hip_stream)
+
+
+def pf8_quant_fwd(x, m, k, ldx, qx, ldqx, sx, ld_sx, qxt, ldqxt, sxt, ld_sxt, w, n, ldw, qw, ldqw, qwt, ldqwt, sw,
+                  ld_sw, hip_stream=0) -> int:
+    return LIB.pf8_quant_fwd(x, m, k, ldx, qx, ldqx, sx, ld_sx, qxt, ldqxt, sxt, ld_sxt, w, n, ldw, qw, ldqw, qwt,
+                             ldqwt, sw, ld_sw, hip_stream)
 
 
 def pf8_quant_w_128x128(w, n, k, ldw, q, ldq, qt, ldqt, dscale, ld_s, hip_stream=0) -> int:

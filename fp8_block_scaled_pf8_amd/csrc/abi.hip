@@ -84,6 +84,27 @@ int pf8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, v
                                               dscale_col, ld_sc, static_cast<hipStream_t>(hip_stream)));
 }
 
+int pf8_quant_fwd(const void* x, int64_t m, int64_t k, int64_t ldx, void* qx, int64_t ldqx, float* sx, int64_t ld_sx,
+                  void* qxt, int64_t ldqxt, float* sxt, int64_t ld_sxt, const void* w, int64_t n, int64_t ldw, void* qw,
+                  int64_t ldqw, void* qwt, int64_t ldqwt, float* sw, int64_t ld_sw, void* hip_stream) {
+  if (x == nullptr || qx == nullptr || sx == nullptr || qxt == nullptr || sxt == nullptr || w == nullptr ||
+      qw == nullptr || sw == nullptr)
+    return PF8_EINVAL;
+  if (m <= 0 || n <= 0 || k <= 0) return PF8_EINVAL;
+  if (m % kGroup != 0 || n % kGroup != 0 || k % kGroup != 0) return PF8_ESHAPE;
+  if (ldx < k || ldqx < k || ld_sx < m || ldqxt < m || ld_sxt < k) return PF8_EINVAL;
+  if (ldw < k || ldqw < k || ld_sw < k / kGroup || (qwt != nullptr && ldqwt < n)) return PF8_EINVAL;
+  if (!aligned16(x) || !aligned16(qx) || !aligned16(qxt) || !aligned4(sx) || !aligned4(sxt)) return PF8_EALIGN;
+  if (!aligned16(w) || !aligned16(qw) || !aligned4(sw) || (qwt != nullptr && !aligned16(qwt))) return PF8_EALIGN;
+  if ((ldx * 2) % 16 != 0 || ldqx % 16 != 0 || ldqxt % 16 != 0 || (ldw * 2) % 16 != 0 || ldqw % 16 != 0 ||
+      (qwt != nullptr && ldqwt % 16 != 0))
+    return PF8_EALIGN;
+  if ((m / kGroup + n / kGroup) * (k / kGroup) > (int64_t{1} << 31) - 1) return PF8_ESHAPE;  // one workgroup per tile
+  if (int s = device_status(); s != PF8_OK) return s;
+  return launch_status(pf8::launch_quant_fwd(x, m, k, ldx, qx, ldqx, sx, ld_sx, qxt, ldqxt, sxt, ld_sxt, w, n, ldw, qw,
+                                             ldqw, qwt, ldqwt, sw, ld_sw, static_cast<hipStream_t>(hip_stream)));
+}
+
 int pf8_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw, void* q, int64_t ldq, void* qt, int64_t ldqt,
                         float* dscale, int64_t ld_s, void* hip_stream) {
   if (w == nullptr || q == nullptr || dscale == nullptr) return PF8_EINVAL;

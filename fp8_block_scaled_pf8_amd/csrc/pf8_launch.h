@@ -13,6 +13,10 @@ hipError_t launch_quant_cols(const void* x, int64_t rows, int64_t cols, int64_t 
 hipError_t launch_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q_row, int64_t ldq_row,
                              float* dscale_row, int64_t ld_sr, void* q_col, int64_t ldq_col, float* dscale_col,
                              int64_t ld_sc, hipStream_t stream);
+hipError_t launch_quant_fwd(const void* x, int64_t m, int64_t k, int64_t ldx, void* qx, int64_t ldqx, float* sx,
+                            int64_t ld_sx, void* qxt, int64_t ldqxt, float* sxt, int64_t ld_sxt, const void* w,
+                            int64_t n, int64_t ldw, void* qw, int64_t ldqw, void* qwt, int64_t ldqwt, float* sw,
+                            int64_t ld_sw, hipStream_t stream);
 hipError_t launch_quant_w(const void* w, int64_t n, int64_t k, int64_t ldw, void* q, int64_t ldq, void* qt,
                           int64_t ldqt, float* dscale, int64_t ld_s, hipStream_t stream);
 

@@ -155,16 +155,14 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
 //   the tile maximum is reduced over the wave and then over the 4 waves in LDS;
 //   codes go straight to q[n][k] (8 bytes per row per thread) and, when qt is requested,
 //   through an LDS tile [128 k][128 n] bytes to qt[k][n].
-__global__ __launch_bounds__(256) void quant_w_kernel(const uint16_t* __restrict__ w, int64_t ldw,
-                                                      uint8_t* __restrict__ q, int64_t ldq,
-                                                      uint8_t* __restrict__ qt, int64_t ldqt,
-                                                      float* __restrict__ dscale, int64_t ld_s) {
-  __shared__ uint32_t red[4];
-  __shared__ __align__(16) uint8_t tile[kGroup * kGroup];
+// (red: 4 words of LDS, tile: kGroup * kGroup bytes of LDS, both owned by the workgroup)
+__device__ __forceinline__ void quant_w_tile(const uint16_t* __restrict__ w, int64_t ldw, uint8_t* __restrict__ q,
+                                             int64_t ldq, uint8_t* __restrict__ qt, int64_t ldqt,
+                                             float* __restrict__ dscale, int64_t ld_s, int64_t tn, int64_t tk,
+                                             uint32_t* red, uint8_t* tile) {
   const int t = threadIdx.x;
   const int rb = t >> 4;  // row block: rows 8*rb .. 8*rb+7
   const int cb = t & 15;  // col block: cols 8*cb .. 8*cb+7
-  const int64_t tn = blockIdx.y, tk = blockIdx.x;
   const int64_t row0 = tn * kGroup + 8 * rb;
   const int64_t col0 = tk * kGroup + 8 * cb;
   uint4 v[8];
@@ -211,6 +209,15 @@ __global__ __launch_bounds__(256) void quant_w_kernel(const uint16_t* __restrict
   }
 }
 
+__global__ __launch_bounds__(256) void quant_w_kernel(const uint16_t* __restrict__ w, int64_t ldw,
+                                                      uint8_t* __restrict__ q, int64_t ldq,
+                                                      uint8_t* __restrict__ qt, int64_t ldqt,
+                                                      float* __restrict__ dscale, int64_t ld_s) {
+  __shared__ uint32_t red[4];
+  __shared__ __align__(16) uint8_t tile[kGroup * kGroup];
+  quant_w_tile(w, ldw, q, ldq, qt, ldqt, dscale, ld_s, blockIdx.y, blockIdx.x, red, tile);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Both orientations from one read: a workgroup takes a 128 x 128 tile, which is 128 row groups
 // (one per row, along the columns) and 128 column groups (one per column, along the rows).
@@ -227,18 +234,17 @@ __device__ __forceinline__ int dual_slot(int c, int s) {
   return (c >> 1) * 256 + 8 * ((s | ((c & 1) << 4)) ^ (((c >> 3) & 7) << 2));
 }
 
-__global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restrict__ x, int64_t ldx,
-                                                         uint8_t* __restrict__ qr, int64_t ldqr,
-                                                         float* __restrict__ sr, int64_t ld_sr,
-                                                         uint8_t* __restrict__ qc, int64_t ldqc,
-                                                         float* __restrict__ sc, int64_t ld_sc) {
-  __shared__ __align__(16) uint32_t red[4][16][4];  // [wave][column chunk][packed column pair]
-  __shared__ __align__(16) uint8_t tile[kGroup * kGroup];
+// (red: [wave][column chunk][packed column pair] words of LDS, tile: kGroup * kGroup bytes of LDS;
+// gc = column group (row mode), gr = row group (col mode))
+__device__ __forceinline__ void quant_dual_tile(const uint16_t* __restrict__ x, int64_t ldx, uint8_t* __restrict__ qr,
+                                                int64_t ldqr, float* __restrict__ sr, int64_t ld_sr,
+                                                uint8_t* __restrict__ qc, int64_t ldqc, float* __restrict__ sc,
+                                                int64_t ld_sc, int64_t gc, int64_t gr, uint32_t (*red)[16][4],
+                                                uint8_t* tile) {
   const int t = threadIdx.x;
   const int rb = t >> 4;  // rows 8*rb .. 8*rb+7 of the tile
   const int cc = t & 15;  // cols 8*cc .. 8*cc+7 of the tile
   const int wave = t >> 6;
-  const int64_t gc = blockIdx.x, gr = blockIdx.y;  // column group (row mode), row group (col mode)
   const int64_t r0 = gr * kGroup, c0 = gc * kGroup;
   uint4 v[8];
 #pragma unroll
@@ -321,6 +327,58 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
   }
 }
 
+__global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                         uint8_t* __restrict__ qr, int64_t ldqr,
+                                                         float* __restrict__ sr, int64_t ld_sr,
+                                                         uint8_t* __restrict__ qc, int64_t ldqc,
+                                                         float* __restrict__ sc, int64_t ld_sc) {
+  __shared__ __align__(16) uint32_t red[4][16][4];
+  __shared__ __align__(16) uint8_t tile[kGroup * kGroup];
+  quant_dual_tile(x, ldx, qr, ldqr, sr, ld_sr, qc, ldqc, sc, ld_sc, blockIdx.x, blockIdx.y, red, tile);
+}
+
+// ---------------------------------------------------------------------------------------------
+// The forward pass's two quantisers in one launch: workgroups [0, nw) take the weight's 128x128
+// tiles, the rest the activation's 128x128 tiles (both groupings). The two tensors are small next
+// to a GEMM's operands (X [8192, 2048] is 32 MB): one launch fills the chip twice as long and
+// pays the launch ramp once.
+struct FwdQuantArgs {
+  const uint16_t* x;
+  int64_t ldx;
+  uint8_t* qx;
+  int64_t ldqx;
+  float* sx;
+  int64_t ld_sx;
+  uint8_t* qxt;
+  int64_t ldqxt;
+  float* sxt;
+  int64_t ld_sxt;
+  int64_t x_col_groups;
+  const uint16_t* w;
+  int64_t ldw;
+  uint8_t* qw;
+  int64_t ldqw;
+  uint8_t* qwt;
+  int64_t ldqwt;
+  float* sw;
+  int64_t ld_sw;
+  int64_t w_col_tiles, w_tiles;
+};
+
+__global__ __launch_bounds__(256) void quant_fwd_kernel(FwdQuantArgs a) {
+  __shared__ __align__(16) uint32_t red[4][16][4];
+  __shared__ __align__(16) uint8_t tile[kGroup * kGroup];
+  const int64_t b = blockIdx.x;  // uniform branch per workgroup
+  if (b < a.w_tiles) {
+    quant_w_tile(a.w, a.ldw, a.qw, a.ldqw, a.qwt, a.ldqwt, a.sw, a.ld_sw, b / a.w_col_tiles, b % a.w_col_tiles,
+                 &red[0][0][0], tile);
+  } else {
+    const int64_t bx = b - a.w_tiles;
+    quant_dual_tile(a.x, a.ldx, a.qx, a.ldqx, a.sx, a.ld_sx, a.qxt, a.ldqxt, a.sxt, a.ld_sxt, bx % a.x_col_groups,
+                    bx / a.x_col_groups, red, tile);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 hipError_t launch_quant_rows(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q, int64_t ldq,
                              float* dscale, int64_t ld_s, hipStream_t stream) {
@@ -353,6 +411,19 @@ hipError_t launch_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t 
   hipLaunchKernelGGL(quant_dual_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(x), ldx,
                      static_cast<uint8_t*>(q_row), ldq_row, dscale_row, ld_sr, static_cast<uint8_t*>(q_col), ldq_col,
                      dscale_col, ld_sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fwd(const void* x, int64_t m, int64_t k, int64_t ldx, void* qx, int64_t ldqx, float* sx,
+                            int64_t ld_sx, void* qxt, int64_t ldqxt, float* sxt, int64_t ld_sxt, const void* w,
+                            int64_t n, int64_t ldw, void* qw, int64_t ldqw, void* qwt, int64_t ldqwt, float* sw,
+                            int64_t ld_sw, hipStream_t stream) {
+  FwdQuantArgs a{static_cast<const uint16_t*>(x), ldx, static_cast<uint8_t*>(qx), ldqx, sx, ld_sx,
+                 static_cast<uint8_t*>(qxt), ldqxt, sxt, ld_sxt, k / kGroup,
+                 static_cast<const uint16_t*>(w), ldw, static_cast<uint8_t*>(qw), ldqw, static_cast<uint8_t*>(qwt),
+                 ldqwt, sw, ld_sw, k / kGroup, (n / kGroup) * (k / kGroup)};
+  const int64_t blocks = a.w_tiles + (m / kGroup) * (k / kGroup);
+  hipLaunchKernelGGL(quant_fwd_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

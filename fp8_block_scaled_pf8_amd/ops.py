@@ -191,8 +191,9 @@ class LinearStep:
               W [N, K] -> tile codes (+ transposed), Y = X . W^T
     backward: dY [M, N] -> codes along N and along M, dX = dY . W, dW = dY^T . X
     With ``fused`` (the default; needs M, N, K multiples of 128) X and dY are each read once by
-    the dual-orientation quantiser: six launches. Otherwise each orientation has its own pass:
-    eight launches. ``run`` enqueues them on the current stream and allocates nothing.
+    the dual-orientation quantiser, and X's and W's quantisers share one launch: five launches.
+    Otherwise each orientation has its own pass: eight launches. ``run`` enqueues them on the
+    current stream and allocates nothing.
     """
 
     def __init__(self, x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, variant: int = L.PF8_GEMM_AUTO,
@@ -231,6 +232,10 @@ class LinearStep:
         quant_x_dual = ("quant_x_dual", lambda: L.pf8_quant_act_dual(
             x.data_ptr(), m, k, x.stride(0), self.qx.data_ptr(), k, self.sx.data_ptr(), m, self.qxt.data_ptr(), m,
             self.sxt.data_ptr(), k, st))
+        quant_fwd = ("quant_x_dual_w_tiles", lambda: L.pf8_quant_fwd(
+            x.data_ptr(), m, k, x.stride(0), self.qx.data_ptr(), k, self.sx.data_ptr(), m, self.qxt.data_ptr(), m,
+            self.sxt.data_ptr(), k, self.w.data_ptr(), n, self.w.stride(0), self.qw.data_ptr(), k,
+            self.qwt.data_ptr(), n, self.sw.data_ptr(), k // GROUP, st))
         quant_w = ("quant_w_tiles", lambda: L.pf8_quant_w_128x128(
             self.w.data_ptr(), n, k, self.w.stride(0), self.qw.data_ptr(), k, self.qwt.data_ptr(), n,
             self.sw.data_ptr(), k // GROUP, st))
@@ -251,7 +256,7 @@ class LinearStep:
             v, L.PF8_WGRAD, n, k, m, self.qdyt.data_ptr(), m, self.sdyt.data_ptr(), n, self.qxt.data_ptr(), m,
             self.sxt.data_ptr(), 1, k, self.dw.data_ptr(), k, st))
         if self.fused:
-            return [quant_x_dual, quant_w, fprop, quant_dy_dual, dgrad, wgrad]
+            return [quant_fwd, fprop, quant_dy_dual, dgrad, wgrad]
         return [quant_x_rows, quant_w, fprop, quant_dy_rows, dgrad, quant_dy_cols, quant_x_cols, wgrad]
 
     def run(self) -> None:

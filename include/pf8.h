@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define PF8_ABI_VERSION 4
+#define PF8_ABI_VERSION 5
 
 /* Status codes (int). */
 #define PF8_OK 0
@@ -93,6 +93,23 @@ int pf8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx, 
 int pf8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx,
                        void* q_row, int64_t ldq_row, float* dscale_row, int64_t ld_sr,
                        void* q_col, int64_t ldq_col, float* dscale_col, int64_t ld_sc, void* hip_stream);
+
+/*
+ * Forward-pass quantisers of one linear layer in one launch [the passages above: X grouped along
+ * K and along the tokens, W by 128x128 tiles with its transposed codes for the data gradient]:
+ * exactly pf8_quant_act_dual(X) and pf8_quant_w_128x128(W), with one workgroup per 128x128 tile
+ * of either tensor.
+ *
+ * X: bf16 [m, k], pitch ldx; qx/sx and qxt/sxt as q_row/dscale_row and q_col/dscale_col of
+ *    pf8_quant_act_dual (qx [m, k], sx[g * ld_sx + r], qxt [k, m], sxt[g * ld_sxt + c]).
+ * W: bf16 [n, k], pitch ldw; qw, qwt (may be NULL), sw as q, qt, dscale of pf8_quant_w_128x128.
+ * m, n and k must be multiples of 128. The outputs are bit-identical to the two separate calls.
+ */
+int pf8_quant_fwd(const void* x, int64_t m, int64_t k, int64_t ldx,
+                  void* qx, int64_t ldqx, float* sx, int64_t ld_sx,
+                  void* qxt, int64_t ldqxt, float* sxt, int64_t ld_sxt,
+                  const void* w, int64_t n, int64_t ldw,
+                  void* qw, int64_t ldqw, void* qwt, int64_t ldqwt, float* sw, int64_t ld_sw, void* hip_stream);
 
 /*
  * 128x128 weight-tile quantiser [paper.rainbus.top summary, section "FP8 块级混合精度训练" and

@@ -25,7 +25,8 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert names == sorted(["pf8_quant_act_1x128", "pf8_quant_act_dual", "pf8_quant_w_128x128", "pf8_block_gemm",
+    assert names == sorted(["pf8_quant_act_1x128", "pf8_quant_act_dual", "pf8_quant_fwd", "pf8_quant_w_128x128",
+                            "pf8_block_gemm",
                             "pf8_block_gemm_variant", "pf8_block_gemm_f32", "pf8_gemm_bf16", "pf8_strerror",
                             "pf8_abi_version"])
     lib = ctypes.CDLL(L.LIB_PATH)
@@ -107,6 +108,32 @@ def test_quant_dual_validation():
     assert _qd(sc=S4 + 2) == L.PF8_EALIGN
     assert _qd(ldx=388) == L.PF8_EALIGN  # 776-byte pitch
     assert _qd(ldqc=264) == L.PF8_EALIGN
+
+
+def _qf(**kw):
+    a = dict(x=A16, m=256, k=384, ldx=384, qx=B16, ldqx=384, sx=S4, ld_sx=256, qxt=C16, ldqxt=256, sxt=S4,
+             ld_sxt=384, w=A16, n=512, ldw=384, qw=B16, ldqw=384, qwt=C16, ldqwt=512, sw=S4, ld_sw=3)
+    a.update(kw)
+    return L.pf8_quant_fwd(a["x"], a["m"], a["k"], a["ldx"], a["qx"], a["ldqx"], a["sx"], a["ld_sx"], a["qxt"],
+                           a["ldqxt"], a["sxt"], a["ld_sxt"], a["w"], a["n"], a["ldw"], a["qw"], a["ldqw"], a["qwt"],
+                           a["ldqwt"], a["sw"], a["ld_sw"], 0)
+
+
+def test_quant_fwd_validation():
+    for key in ["x", "qx", "sx", "qxt", "sxt", "w", "qw", "sw"]:
+        assert _qf(**{key: 0}) == L.PF8_EINVAL, key
+    assert _qf(m=0) == L.PF8_EINVAL
+    assert _qf(m=200) == L.PF8_ESHAPE
+    assert _qf(n=200) == L.PF8_ESHAPE
+    assert _qf(k=200, ldx=384, ldw=384) == L.PF8_ESHAPE
+    assert _qf(ldx=256) == L.PF8_EINVAL
+    assert _qf(ld_sx=128) == L.PF8_EINVAL
+    assert _qf(ldqxt=128) == L.PF8_EINVAL
+    assert _qf(ld_sw=2) == L.PF8_EINVAL
+    assert _qf(ldqwt=256) == L.PF8_EINVAL
+    assert _qf(x=A16 + 2) == L.PF8_EALIGN
+    assert _qf(qwt=C16 + 4) == L.PF8_EALIGN
+    assert _qf(ldw=388) == L.PF8_EALIGN
 
 
 def _qw(**kw):
@@ -219,6 +246,8 @@ def test_no_device_is_reported_after_validation():
     assert _gm(m=1, n=3, ld_as=1, ldd=8) == L.PF8_ENODEV  # ragged M and N are accepted
     assert _qa() == L.PF8_ENODEV
     assert _qd() == L.PF8_ENODEV
+    assert _qf() == L.PF8_ENODEV
+    assert _qf(qwt=0, ldqwt=0) == L.PF8_ENODEV
     assert _gf() == L.PF8_ENODEV
     assert _gb() == L.PF8_ENODEV
     assert _gf(accumulate=0, m=3, n=5, ld_as=3, ldd=8) == L.PF8_ENODEV

@@ -285,12 +285,12 @@ def test_padded_output_and_strided_operands(variant):
 
 @pytest.mark.parametrize("fused", [True, False], ids=["dual_quant", "single_quant"])
 def test_linear_step_matches_oracle(fused):
-    """The whole layer pass used by the benchmark on the tiny shape, with the dual-orientation
-    quantiser (6 launches) and with one quantiser pass per orientation (8 launches)."""
+    """The whole layer pass used by the benchmark on the tiny shape, with the fused quantisers (5
+    launches) and with one quantiser pass per orientation (8 launches)."""
     t = generate("tiny_fprop")
     dyb = _rand_bits((256, 384), 41, 1e-3, outliers=False)
     step = pf8.LinearStep(to_dev_bf16(t["X"]), to_dev_bf16(t["W"]), to_dev_bf16(dyb), fused=fused)
-    assert len(step.launches()) == (6 if fused else 8)
+    assert len(step.launches()) == (5 if fused else 8)
     step.run()
     torch.cuda.synchronize()
     qx, sx = oracle.quant_act_1x128(t["X"], "cols")

@@ -228,3 +228,29 @@ def test_dual_rejects_ragged_shapes():
     x = torch.zeros((200, 256), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(RuntimeError, match="unsupported shape"):
         pf8.quant_act_dual(x)
+
+
+@pytest.mark.parametrize("m,n,k", [(128, 128, 128), (256, 384, 512), (1024, 640, 256)])
+def test_fwd_quantiser_matches_separate_calls_and_oracle(m, n, k):
+    """pf8_quant_fwd: X's dual quantisation and W's tile quantisation in one launch."""
+    rng = np.random.default_rng(m + n + k)
+    xb = f32_to_bf16_bits((rng.standard_normal((m, k)) * 2).astype(np.float32))
+    wb = f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    x, w = to_dev_bf16(xb), to_dev_bf16(wb)
+    e = lambda *sh, dt=torch.uint8: torch.full(sh, 0x77, dtype=dt, device=DEV)  # noqa: E731
+    qx, sx, qxt, sxt = e(m, k), e(k // 128, m, dt=torch.float32), e(k, m), e(m // 128, k, dt=torch.float32)
+    qw, qwt, sw = e(n, k), e(k, n), e(n // 128, k // 128, dt=torch.float32)
+    pf8._lib.check(pf8.pf8_quant_fwd(x.data_ptr(), m, k, k, qx.data_ptr(), k, sx.data_ptr(), m, qxt.data_ptr(), m,
+                                     sxt.data_ptr(), k, w.data_ptr(), n, k, qw.data_ptr(), k, qwt.data_ptr(), n,
+                                     sw.data_ptr(), k // 128, torch.cuda.current_stream().cuda_stream))
+    r_qx, r_sx, r_qxt, r_sxt = pf8.quant_act_dual(x)
+    r_qw, r_qwt, r_sw = pf8.quant_w_128x128(w)
+    torch.cuda.synchronize()
+    for got, want in ((qx, r_qx), (qxt, r_qxt), (qw, r_qw), (qwt, r_qwt)):
+        assert torch.equal(got, want)
+    for got, want in ((sx, r_sx), (sxt, r_sxt), (sw, r_sw)):
+        assert torch.equal(got.view(torch.int32), want.view(torch.int32))
+    o_qx, o_sx = oracle.quant_act_1x128(xb, "cols")
+    o_qw, o_qwt, o_sw = oracle.quant_w_128x128(wb)
+    assert np.array_equal(u8(qx), o_qx) and np.array_equal(f32(sx), o_sx)
+    assert np.array_equal(u8(qw), o_qw) and np.array_equal(u8(qwt), o_qwt) and np.array_equal(f32(sw), o_sw)
