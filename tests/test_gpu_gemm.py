@@ -443,3 +443,32 @@ def test_gemm_bf16_padded_pitches():
     assert np.all(bits[:, n:] == canary)
     _report((bits[:, :n].astype(np.uint32) << 16).view(np.float32).astype(np.float64),
             oracle.unquantized_reference(ab, bb), "bf16 padded")
+
+
+def test_full_size_bf16_and_f32_gemms_sampled():
+    """The comparison BF16 GEMM on the fprop shape and the FP32 weight gradient accumulated into a
+    main gradient on the layer step's wgrad shape, at full size, on sampled output rows."""
+    rng = np.random.default_rng(61)
+    m, n, k = 8192, 12288, 2048
+    ab = f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    bb = f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    d = pf8.gemm_bf16(to_dev_bf16(ab), to_dev_bf16(bb))
+    torch.cuda.synchronize()
+    rows = _sample_rows(m, 96, 62)
+    _report(bf16_f64(d)[rows], oracle.unquantized_reference(ab[rows], bb), "bf16 8192x12288x2048")
+    del d
+    # wgrad of the layer step: dW [12288, 2048] = dY^T X over 8192 tokens, FP32, accumulated twice
+    t = generate("mlp_gateup_layer_step", only=["X", "dY"])
+    qdyt, sdyt = pf8.quant_act_1x128(to_dev_bf16(t["dY"]), "rows")
+    qxt, sxt = pf8.quant_act_1x128(to_dev_bf16(t["X"]), "rows")
+    base = torch.full((12288, 2048), 0.25, dtype=torch.float32, device=DEV)
+    pf8.wgrad_f32(qdyt, sdyt, qxt, sxt, out=base, accumulate=True)
+    pf8.wgrad_f32(qdyt, sdyt, qxt, sxt, out=base, accumulate=True)
+    torch.cuda.synchronize()
+    cols = _sample_rows(12288, 96, 63)
+    r_qdyt, r_sdyt = oracle.quant_act_1x128(np.ascontiguousarray(t["dY"][:, cols]), "rows")
+    r_qxt, r_sxt = oracle.quant_act_1x128(t["X"], "rows")
+    ref = 0.25 + 2.0 * oracle.gemm_wgrad(r_qdyt, r_sdyt, r_qxt, r_sxt)
+    got = base.cpu().numpy()[cols].astype(np.float64)
+    rep = oracle.gemm_tolerance_report(got, ref)
+    assert rep["violations"] == 0, rep

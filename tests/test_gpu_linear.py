@@ -80,3 +80,22 @@ def test_fp8_linear_rejects_ragged_tokens():
     w = torch.zeros((128, 256), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(ValueError, match="multiples of 128"):
         pf8.fp8_linear(x, w)
+
+
+def test_fp8_linear_noncontiguous_input():
+    """A transposed-view input, made contiguous by the layer before quantisation."""
+    m, k, n = 256, 384, 128
+    xb = _bits((k, m), 31, 1.0, True)   # stored transposed: X = xt^T
+    wb = _bits((n, k), 32, 0.02, False)
+    dyb = _bits((m, n), 33, 1e-3, False)
+    xt = to_dev_bf16(xb)
+    x = xt.t().requires_grad_(True)     # [m, k] view with strides (1, m)
+    w = to_dev_bf16(wb).requires_grad_(True)
+    y = pf8.fp8_linear(x, w)
+    y.backward(to_dev_bf16(dyb))
+    torch.cuda.synchronize()
+    x_bits = np.ascontiguousarray(xb.T)
+    ry, rdx, rdw = _oracle_layer(x_bits, wb, dyb)
+    _check(bf16_f64(y.detach()), ry, "Y")
+    _check(bf16_f64(x.grad.contiguous()), rdx, "dX")
+    _check(bf16_f64(w.grad), rdw, "dW")
