@@ -292,8 +292,13 @@ def summarize_prof(dirs):
             seq = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in pf8_rows]
             dual = any("quant_fwd" in r["Kernel_Name"] for r in pf8_rows)
             kernels = KERNELS_FUSED if dual else KERNELS_UNFUSED
-            nsteps = len(seq) // len(kernels)
-            if nsteps >= 3 and len(seq) % len(kernels) == 0:
+            # the step's launches come first; later launches (the FP32-accumulate timing) end the run
+            names = [r["Kernel_Name"] for r in pf8_rows]
+            nsteps = 0
+            while (nsteps + 1) * len(kernels) <= len(names) and \
+                    names[nsteps * len(kernels):(nsteps + 1) * len(kernels)] == names[:len(kernels)]:
+                nsteps += 1
+            if nsteps >= 3:
                 skip = 2  # warm-up steps
                 for j, name in enumerate(kernels):
                     v = [seq[i * len(kernels) + j] for i in range(skip, nsteps)]
