@@ -49,9 +49,10 @@ def parse_args():
     ap.add_argument("--unfused", action="store_true", help="one quantiser pass per orientation (eight launches)")
     ap.add_argument("--no-configs", action="store_true", help="skip timing the per-configuration GEMMs")
     ap.add_argument("--no-comparators", action="store_true", help="skip timing hipBLASLt on the fprop shape")
-    ap.add_argument("--only", choices=["fprop_gemm", "quant_dy_dual", "copy"], default=None,
-                    help="profiling modes: run only the headline fprop GEMM, only the dual-orientation dY "
-                         "quantiser, or only a 1 GiB device copy (the calibration kernel for the FETCH_SIZE / "
+    ap.add_argument("--only", choices=["fprop_gemm", "hipblaslt_fp8", "quant_dy_dual", "copy"], default=None,
+                    help="profiling modes: run only the headline fprop GEMM, hipBLASLt's FP8 GEMM on the same "
+                         "E4M3 codes (per-tensor unit scales, for counter comparisons), only the dual-orientation "
+                         "dY quantiser, or only a 1 GiB device copy (the calibration kernel for the FETCH_SIZE / "
                          "WRITE_SIZE counters), --steps times")
     ap.add_argument("--summarize-prof", nargs="+", metavar="DIR", default=None,
                     help="print a text summary of rocprofv3 csv output directories and exit")
@@ -266,10 +267,18 @@ def only_mode(args, torch, pf8):
     qx, sx = pf8.quant_act_1x128(_dev_bf16(t["X"], torch), "cols")
     qw, _, sw = pf8.quant_w_128x128(_dev_bf16(t["W"], torch), transposed=False)
     y = torch.empty((qx.shape[0], qw.shape[0]), dtype=torch.bfloat16, device="cuda:0")
-    for _ in range(args.steps):
-        pf8.fprop(qx, sx, qw, sw, out=y)
+    if args.only == "hipblaslt_fp8":
+        # context for counter comparisons: hipBLASLt's FP8 GEMM (one unit scale per tensor) on the
+        # very same E4M3 codes
+        a8, b8 = qx.view(torch.float8_e4m3fn), qw.view(torch.float8_e4m3fn)
+        one = torch.ones((), device="cuda:0")
+        for _ in range(args.steps):
+            torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+    else:
+        for _ in range(args.steps):
+            pf8.fprop(qx, sx, qw, sw, out=y)
     torch.cuda.synchronize()
-    print(json.dumps({"only": "fprop_gemm", "m": qx.shape[0], "n": qw.shape[0], "k": qx.shape[1],
+    print(json.dumps({"only": args.only, "m": qx.shape[0], "n": qw.shape[0], "k": qx.shape[1],
                       "launches": args.steps, "gemm_source_sha256_16": gemm_source_hash()}), flush=True)
 
 
