@@ -5,21 +5,18 @@
 // and weight-gradient GEMMs take blockwise E4M3 operands; the product of the two block scales is
 // applied once per 128-wide K block and the result accumulates in FP32 and is written as BF16.
 //
-// Structure (one code path per variant, gfx950 only):
-//  * 256 threads = 4 waves in a 2x2 grid; the workgroup owns a BM x BN macro-tile of D and walks
-//    K in 128-wide blocks (one scale block per step).
-//  * A and B block tiles (BM x 128 and BN x 128 bytes) are fetched with 16-byte buffer loads
-//    (out-of-range rows of a ragged edge tile read as zero) one block ahead into registers and
-//    written to a double-buffered LDS ring; 16-byte chunk c of LDS row r sits at chunk
-//    c ^ (r & 7), so the MFMA operand reads of 8 consecutive rows hit distinct banks.
-//  * MX variant: v_mfma_scale_f32_32x32x64_f8f6f4. The scales are powers of two, so their
-//    exponent bytes are exact E8M0 scale operands and the matrix core applies sa*sb itself while
-//    accumulating in FP32 (the gfx950 counterpart of a block-scaled tensor-core path).
-//  * PROMOTE variant: v_mfma_f32_16x16x128_f8f6f4 covers one whole 128-wide scale block per
-//    instruction; it runs with a zero accumulator and the FP32 partial is folded into the
-//    running accumulator with one FMA by sa*sb per element.
-//  * The MFMA takes B as its first operand, so each lane ends up owning 4 consecutive output
-//    columns of one row: the epilogue converts to BF16 (RNE) and stores 8 bytes per lane.
+// Two kernels, one code path each (gfx950 only):
+//  * gemm_mx_kernel (the default): 256 threads = 4 waves in a 2x2 grid own a BM x BN tile of D.
+//    Operands stream into a ring of five LDS stage buffers by direct-to-LDS buffer loads, and
+//    v_mfma_scale_f32_32x32x64_f8f6f4 applies the block scales while it accumulates in FP32: the
+//    scales are powers of two, so their exponent bytes are exact E8M0 scale operands (the gfx950
+//    counterpart of a block-scaled tensor-core path). The BF16 tile leaves through LDS as whole
+//    rows; an FP32 form writes (or adds to) an FP32 result. Details above the kernel.
+//  * gemm_promote_kernel: register-staged, double-buffered LDS; one v_mfma_f32_16x16x128_f8f6f4
+//    covers a whole 128-wide scale block with a zero accumulator, and its FP32 partial is folded
+//    into the running accumulator with one FMA by sa*sb per element.
+//  * Both take B as the MFMA's first operand, so each lane owns consecutive output columns of
+//    one row.
 //  * Workgroup ids are remapped so each XCD (ids are dealt round-robin over 8) works on a
 //    contiguous range of tiles, walked in groups of 8 tile-rows for L2 reuse of A and B panels.
 #include "pf8_device.h"
@@ -80,8 +77,8 @@ __device__ __forceinline__ void store4(uint16_t* __restrict__ d, int64_t ldd, in
   }
 }
 
-template <int BM, int BN, bool ROW_B, bool MX, bool EDGE>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+template <int BM, int BN, bool ROW_B, bool EDGE>
+__global__ __launch_bounds__(256) void gemm_promote_kernel(GemmArgs p, int tiles_m, int tiles_n) {
   constexpr int WM = BM / 2, WN = BN / 2;  // wave tile (2 x 2 waves)
   constexpr int A_BYTES = BM * kGroup, B_BYTES = BN * kGroup, STAGE = A_BYTES + B_BYTES;
   constexpr int A_LOADS = BM / 32, B_LOADS = BN / 32;  // 16-byte chunks per thread per K block
@@ -158,96 +155,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p, int tiles_m, int 
     return static_cast<int64_t>(kb) * p.ld_as + i;
   };
 
-  if constexpr (MX) {
-    // ================= MX variant: 32x32x64 block-scaled MFMA =================
-    constexpr int TM = WM / 32, TN = WN / 32;
-    v16f acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    // lane's scale rows: A row m0 + wm*WM + 32i + lane%32, B row n0 + wn*WN + 32j + lane%32
-    const int l32 = lane & 31, half = lane >> 5;
-    const int64_t a_row0 = m0 + wm * WM + l32, b_row0 = n0 + wn * WN + l32;
-    // raw fp32 scale bits; the E8M0 exponent byte (bits 23..30) is extracted where it is used,
-    // so the prefetch does not have to complete before this block's MFMAs are issued
-    uint32_t sa_raw[TM], sb_raw[TN], sa_nxt[TM], sb_nxt[TN];
-    auto load_scales = [&](int kb, uint32_t (&sa)[TM], uint32_t (&sb)[TN]) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) sa[i] = __float_as_uint(p.a_dscale[a_scale_idx(kb, a_row0 + 32 * i)]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) sb[j] = __float_as_uint(p.b_dscale[b_scale_idx(kb, b_row0 + 32 * j)]);
-    };
-    const int ra_row0 = wm * WM + l32, rb_row0 = wn * WN + l32;
-    const int sw = l32 & 7;  // (row & 7) for every fragment row this lane reads
-
-    gload(0);
-    load_scales(0, sa_raw, sb_raw);
-    lds_store(0);
-    __syncthreads();
-    for (int kb = 0; kb < nk; ++kb) {
-      const bool more = kb + 1 < nk;
-      if (more) {
-        gload(kb + 1);
-        load_scales(kb + 1, sa_nxt, sb_nxt);
-      }
-      int sae[TM], sbe[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) sae[i] = static_cast<int>(sa_raw[i] >> 23);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) sbe[j] = static_cast<int>(sb_raw[j] >> 23);
-      const uint8_t* sa = smem + (kb & 1) * STAGE;
-      const uint8_t* sb = sa + A_BYTES;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int c0 = ((4 * s + 2 * half) ^ sw) << 4, c1 = ((4 * s + 2 * half + 1) ^ sw) << 4;
-        v8i fa[TM], fb[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int row = ra_row0 + 32 * i;
-          fa[i] = lds_read32(sa, row * kGroup + c0, row * kGroup + c1);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int row = rb_row0 + 32 * j;
-          fb[j] = lds_read32(sb, row * kGroup + c0, row * kGroup + c1);
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0, sbe[j], 0,
-                                                                        sae[i]);
-      }
-      // keep the MFMAs ahead of the LDS refill, which has to wait for the prefetch to land
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) lds_store((kb + 1) & 1);
-      __syncthreads();
-      if (more) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) sa_raw[i] = sa_nxt[i];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) sb_raw[j] = sb_nxt[j];
-      }
-    }
-    // epilogue: lane owns D[m][n .. n+3] with m = lane%32 of the tile, n = 8*(r/4) + 4*(lane/32)
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t m = m0 + wm * WM + 32 * i + l32;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int64_t n = n0 + wn * WN + 32 * j + 8 * q4 + 4 * half;
-          store4<EDGE>(p.d, p.ldd, m, n, M, N, acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
-                       acc[i][j][4 * q4 + 3]);
-        }
-      }
-  } else {
-    // ================= PROMOTE variant: 16x16x128 MFMA per scale block + FP32 FMA =================
+  {
+    // 16x16x128 MFMA per scale block + FP32 FMA
     constexpr int TM = WM / 16, TN = WN / 16;
     v4f acc[TM][TN];
 #pragma unroll
@@ -814,9 +723,9 @@ static hipError_t launch_tile(const GemmArgs& args, hipStream_t stream) {
     }
   } else {
     if (edge)
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, ROW_B, false, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
+      hipLaunchKernelGGL((gemm_promote_kernel<BM, BN, ROW_B, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
     else
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, ROW_B, false, false>), grid, block, 0, stream, args, tiles_m, tiles_n);
+      hipLaunchKernelGGL((gemm_promote_kernel<BM, BN, ROW_B, false>), grid, block, 0, stream, args, tiles_m, tiles_n);
   }
   return hipGetLastError();
 }
