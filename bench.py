@@ -144,6 +144,60 @@ def time_comparators(torch, pf8, m, n, k, reps=20):
     return {"shape": [m, n, k], "note": "library GEMMs without block scales; context only", **out}
 
 
+def device_peak_fp8():
+    """Dense FP8 MFMA peak from the device itself: compute units x max engine clock x 8192 FLOP per
+    clock and CU (rocminfo's GPU agent), beside the published figure. None if rocminfo is unavailable."""
+    import re
+    import subprocess
+
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except Exception:  # pragma: no cover - depends on the host
+        return None
+    for agent in re.split(r"\n(?=\*+\s*\n\s*Agent \d+)", out):
+        name = re.search(r"^\s*Name:\s*(\S+)", agent, re.M)
+        cus = re.search(r"Compute Unit:\s*(\d+)", agent)
+        mhz = re.search(r"Max Clock Freq\. \(MHz\):\s*(\d+)", agent)
+        if name and name.group(1).startswith("gfx") and cus and mhz:
+            tflops = int(cus.group(1)) * int(mhz.group(1)) * 1e6 * 8192 / 1e12
+            return {"arch": name.group(1), "cus": int(cus.group(1)), "max_clock_mhz": int(mhz.group(1)),
+                    "tflops": round(tflops, 1), "source": "rocminfo: CUs x max clock x 8192 FLOP/clk/CU"}
+    return None
+
+
+def time_cold_warm(torch, fn, reps=20, flush_bytes=512 << 20):
+    """One kernel launch timed with events, cold (reading a flush_bytes buffer evicts L2 and the 256 MB
+    Infinity Cache before every launch, outside the events; a read leaves no dirty lines whose
+    write-back would be charged to the kernel) and warm (back to back)."""
+    import fp8_block_scaled_pf8_amd._lib as L
+
+    scratch = torch.ones(flush_bytes, dtype=torch.uint8, device="cuda:0")
+    st = torch.cuda.current_stream()
+    pairs = {"cold": [], "warm": []}
+    for _ in range(reps):
+        scratch.max()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        L.check(fn(), "cold launch")
+        e1.record(st)
+        pairs["cold"].append((e0, e1))
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        L.check(fn(), "warm launch")
+        e1.record(st)
+        pairs["warm"].append((e0, e1))
+    torch.cuda.synchronize()
+    del scratch
+    out = {}
+    for kind, evs in pairs.items():
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        out[f"{kind}_us_median"] = round(float(np.median(us)), 2)
+        out[f"{kind}_us_p10"] = round(float(np.percentile(us, 10)), 2)
+        out[f"{kind}_us_p90"] = round(float(np.percentile(us, 90)), 2)
+    return out
+
+
 def time_config_gemms(pf8, torch, reps=20):
     """Average kernel time of each configured GEMM (inputs quantised on the GPU first)."""
     from workloads import WORKLOADS, generate
@@ -361,10 +415,13 @@ def main():
     ms_step_wall = wall * 1e3 / args.steps
     # per-kernel averages from the events (same stream as the launches)
     per = {name: 0.0 for name in names}
+    per_all = {name: [] for name in names}
     gpu_ms = 0.0
     for e in evs:
         for j, name in enumerate(names):
-            per[name] += e[j].elapsed_time(e[j + 1])
+            dt = e[j].elapsed_time(e[j + 1])
+            per[name] += dt
+            per_all[name].append(dt * 1e3)
         gpu_ms += e[0].elapsed_time(e[-1])
     per = {kname: v / args.steps for kname, v in per.items()}
     ms_step = gpu_ms / args.steps
@@ -373,7 +430,9 @@ def main():
     kernels = {}
     for name in names:
         ms = per[name]
-        entry = {"us": round(ms * 1e3, 2)}
+        entry = {"us": round(ms * 1e3, 2), "us_median": round(float(np.median(per_all[name])), 2),
+                 "us_p10": round(float(np.percentile(per_all[name], 10)), 2),
+                 "us_p90": round(float(np.percentile(per_all[name], 90)), 2)}
         if name.endswith("gemm"):
             tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
             entry.update(tflops=round(tf, 1), frac_peak=round(tf / PEAK_FP8_TFLOPS, 4))
@@ -395,6 +454,13 @@ def main():
     torch.cuda.synchronize()
     f32_us = e0.elapsed_time(e1) * 1e3 / 20
     del main_grad
+    # cold-cache (L2 and Infinity Cache evicted before every launch) against warm timing of the
+    # headline GEMM and of the dY quantiser, on the step's own buffers
+    thunks = dict(step.launches())
+    cache = {"flush_bytes": 512 << 20}
+    for name in ("fprop_gemm", "quant_dy_dual"):
+        if name in thunks:
+            cache[name] = time_cold_warm(torch, thunks[name])
     fp_ms = per["fprop_gemm"]
     achieved = 2.0 * m * n * k / (fp_ms * 1e-3) / 1e12
     traffic = measured_traffic() if args.variant == "auto" else None
@@ -416,6 +482,8 @@ def main():
         "kernels": kernels,
         "wgrad_f32_accumulate": {"us": round(f32_us, 2), "tflops": round(2.0 * m * n * k / (f32_us * 1e-6) / 1e12, 1),
                                  "note": "dW in FP32 added to a main gradient (not part of the step)"},
+        "cache": cache,
+        "peak_device": device_peak_fp8(),
     }
     del step, x, w, dy
     torch.cuda.empty_cache()

@@ -1,0 +1,107 @@
+"""Host logic of bench.py (no GPU): the one-GPU contract, the algorithmic byte counts behind the
+roofline figures, the device-peak parser and the per-launch-position profile summary."""
+import csv
+import importlib.util
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr
+
+
+def test_algorithmic_bytes():
+    b = _bench()
+    m, n, k, g = 8192, 12288, 2048, 128
+    # GEMM: both code operands once, the BF16 result, the activation scales (one per row and K block)
+    # and the weight tile scales
+    assert b._alg_bytes("fprop_gemm", m, n, k) == m * k + n * k + 2 * m * n + (k // g) * m * 4 + (n // g) * (k // g) * 4
+    assert b._alg_bytes("fprop_gemm", m, n, k) == 243_800_064  # 243.8 MB, the headline GEMM's figure
+    # dual quantiser: one BF16 read, two code sets and two scale sets written
+    assert b._alg_bytes("quant_dy_dual", m, n, k) == 2 * m * n + 2 * (m * n + (m * n // g) * 4)
+    # weight tiles: BF16 read, codes and transposed codes, one scale per 128x128 tile
+    assert b._alg_bytes("quant_w_tiles", m, n, k) == 2 * n * k + 2 * n * k + (n * k // (g * g)) * 4
+    # the fused forward quantiser moves exactly what its two parts move
+    assert b._alg_bytes("quant_x_dual_w_tiles", m, n, k) == (b._alg_bytes("quant_x_dual", m, n, k)
+                                                             + b._alg_bytes("quant_w_tiles", m, n, k))
+
+
+_ROCMINFO = """*******
+Agent 1
+*******
+  Name:                    AMD EPYC 9575F 64-Core Processor
+  Marketing Name:          AMD EPYC 9575F 64-Core Processor
+  Compute Unit:            128
+  Max Clock Freq. (MHz):   3300
+*******
+Agent 2
+*******
+  Name:                    gfx950
+  Marketing Name:          AMD Instinct MI355X
+  Compute Unit:            256
+  Max Clock Freq. (MHz):   2400
+  ISA Info:
+    ISA 1
+      Name:                    amdgcn-amd-amdhsa--gfx950:sramecc+:xnack-
+"""
+
+
+def test_device_peak_from_rocminfo(monkeypatch):
+    b = _bench()
+
+    class Out:
+        stdout = _ROCMINFO
+
+    monkeypatch.setattr(subprocess, "run", lambda *a, **kw: Out())
+    peak = b.device_peak_fp8()
+    assert peak["arch"] == "gfx950" and peak["cus"] == 256 and peak["max_clock_mhz"] == 2400
+    assert peak["tflops"] == 5033.2  # 256 CUs x 2.4 GHz x 8192 FLOP per clock and CU
+
+    def missing(*a, **kw):
+        raise FileNotFoundError("rocminfo")
+
+    monkeypatch.setattr(subprocess, "run", missing)
+    assert b.device_peak_fp8() is None
+
+
+def test_profile_summary_step_positions(tmp_path, capsys):
+    """The per-position view takes the leading run of whole steps and stops at other launches."""
+    b = _bench()
+    step = ["pf8::quant_fwd_kernel(pf8::FwdQuantArgs)",
+            "void pf8::gemm_mx_kernel<256, 256, false, false, 5, false, false>(pf8::GemmArgs, int, int)",
+            "pf8::quant_dual_kernel(unsigned short const*)",
+            "void pf8::gemm_mx_kernel<256, 256, false, false, 5, false, false>(pf8::GemmArgs, int, int)",
+            "void pf8::gemm_mx_kernel<192, 256, true, false, 5, false, false>(pf8::GemmArgs, int, int)"]
+    rows, t = [], 0
+    for i in range(4):  # 4 steps: 2 warm-up + 2 counted
+        for j, name in enumerate(step):
+            dur = 1000 * (j + 1) + i
+            rows.append({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur})
+            t += dur + 10
+    for _ in range(2):  # FP32-accumulate launches after the step, not part of it
+        rows.append({"Kernel_Name": "void pf8::gemm_mx_kernel<192, 256, true, true, 5, true, false>(...)",
+                     "Start_Timestamp": t, "End_Timestamp": t + 99999})
+        t += 100009
+    with open(tmp_path / "step_kernel_trace.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        wr.writeheader()
+        wr.writerows(rows)
+    b.summarize_prof([str(tmp_path)])
+    lines = [ln for ln in capsys.readouterr().out.splitlines() if ln.startswith("step position")]
+    assert [ln.split(":")[0].split()[-1] for ln in lines] == b.KERNELS_FUSED
+    for j, ln in enumerate(lines):
+        assert "dispatches=2" in ln
+        assert f"avg_ns={1000 * (j + 1) + 2.5:.0f}" in ln or f"avg_ns={1000 * (j + 1) + 2}" in ln
