@@ -265,8 +265,14 @@ def cpu_baseline(sample_tokens=8192):
     oracle.gemm_wgrad(qdyt, sdyt, qxt, sxt)
     dt = time.perf_counter() - t0
     flops = 3 * 2.0 * m * n * k
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:  # pragma: no cover - not Linux
+        pass
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 2),
+            "seconds": round(dt, 2), "cpu_model": cpu_model,
             "sample": f"the same layer pass (quantisers and the three GEMMs, float64 oracle) on {m} of the 8192 tokens: "
                       f"X [{m},{k}], W [{n},{k}], dY [{m},{n}]; host cpus={os.cpu_count()} "
                       f"affinity={len(os.sched_getaffinity(0))}"}
