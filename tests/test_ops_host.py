@@ -1,0 +1,15 @@
+"""Host-side layout choices of the Python binding (no GPU needed)."""
+import fp8_block_scaled_pf8_amd.ops as ops
+
+
+def test_code_pitch():
+    # odd multiples of 4 KiB get 128 more bytes, every other width is kept
+    assert ops.code_pitch(12288) == 12416
+    assert ops.code_pitch(4096) == 4224
+    assert ops.code_pitch(20480) == 20608
+    for cols in (128, 384, 2048, 6144, 8192, 16384):
+        assert ops.code_pitch(cols) == cols
+    # rows stay 128-byte aligned (the quantisers and the GEMM move whole 128-byte lines)
+    for cols in range(128, 65536 + 1, 128):
+        p = ops.code_pitch(cols)
+        assert p >= cols and p % 128 == 0 and p - cols in (0, 128)
