@@ -220,7 +220,7 @@ def time_config_gemms(pf8, torch, reps=20):
                 qdyt, sdyt = pf8.quant_act_1x128(dev["dY"], "rows")
                 qxt, sxt = pf8.quant_act_1x128(dev["X"], "rows")
                 fn = lambda a=qdyt, sa=sdyt, b=qxt, sb=sxt: pf8.wgrad(a, sa, b, sb, out=y)  # noqa: E731
-            y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+            y = pf8.ops.result_buffer(m, n, torch.bfloat16, "cuda:0")
             for _ in range(3):
                 fn()
             st = torch.cuda.current_stream()
@@ -326,7 +326,7 @@ def only_mode(args, torch, pf8):
     t = generate(WORKLOAD, only=["X", "W"])
     qx, sx = pf8.quant_act_1x128(_dev_bf16(t["X"], torch), "cols")
     qw, _, sw = pf8.quant_w_128x128(_dev_bf16(t["W"], torch), transposed=False)
-    y = torch.empty((qx.shape[0], qw.shape[0]), dtype=torch.bfloat16, device="cuda:0")
+    y = pf8.ops.result_buffer(qx.shape[0], qw.shape[0], torch.bfloat16, "cuda:0")  # the step's layout
     if args.only == "hipblaslt_fp8":
         # context for counter comparisons: hipBLASLt's FP8 GEMM (one unit scale per tensor) on the
         # very same E4M3 codes

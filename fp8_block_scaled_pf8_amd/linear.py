@@ -45,7 +45,9 @@ class Fp8LinearFunction(torch.autograd.Function):
         _check_shapes(x2.shape[0], n, k)
         qx, sx, qxt, sxt = ops.quant_act_dual(x2)
         qw, qwt, sw = ops.quant_w_128x128(w.contiguous(), transposed=True)
-        y = ops.fprop(qx, sx, qw, sw)
+        # results handed to the caller are plain contiguous tensors (the library's own workspaces
+        # use padded row pitches instead)
+        y = ops.fprop(qx, sx, qw, sw, out=torch.empty((x2.shape[0], n), dtype=torch.bfloat16, device=x.device))
         ctx.save_for_backward(qxt, sxt, qwt, sw)
         ctx.lead, ctx.k, ctx.main_grad = lead, k, main_grad
         return y.reshape(*lead, n)
@@ -62,11 +64,12 @@ class Fp8LinearFunction(torch.autograd.Function):
         qdy, sdy, qdyt, sdyt = ops.quant_act_dual(dy2)
         dx = dw = None
         if ctx.needs_input_grad[0]:
-            dx = ops.dgrad(qdy, sdy, qwt, sw).reshape(*ctx.lead, ctx.k)
+            dx = ops.dgrad(qdy, sdy, qwt, sw, out=torch.empty((dy2.shape[0], ctx.k), dtype=torch.bfloat16,
+                                                              device=dy2.device)).reshape(*ctx.lead, ctx.k)
         if ctx.main_grad is not None:
             ops.wgrad_f32(qdyt, sdyt, qxt, sxt, out=ctx.main_grad, accumulate=True)
         elif ctx.needs_input_grad[1]:
-            dw = ops.wgrad(qdyt, sdyt, qxt, sxt)
+            dw = ops.wgrad(qdyt, sdyt, qxt, sxt, out=torch.empty((n, ctx.k), dtype=torch.bfloat16, device=dy2.device))
         return dx, dw, None
 
 

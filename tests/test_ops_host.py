@@ -13,3 +13,18 @@ def test_code_pitch():
     for cols in range(128, 65536 + 1, 128):
         p = ops.code_pitch(cols)
         assert p >= cols and p % 128 == 0 and p - cols in (0, 128)
+
+
+def test_out_pitch():
+    # BF16 results: 16-byte rows, 128 more bytes when the row is a multiple of 4 KiB
+    assert ops.out_pitch(12288, 2) == 12352
+    assert ops.out_pitch(2048, 2) == 2112
+    assert ops.out_pitch(384, 2) == 384
+    assert ops.out_pitch(5407, 2) == 5408
+    # FP32 results
+    assert ops.out_pitch(2048, 4) == 2080
+    assert ops.out_pitch(384, 4) == 384
+    for eb in (2, 4):
+        for cols in range(1, 9000, 7):
+            p = ops.out_pitch(cols, eb)
+            assert p >= cols and (p * eb) % 16 == 0 and (p * eb) % 4096 != 0
