@@ -610,35 +610,78 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
 #undef PF8_WAIT_VM_LGKM0
 
   if constexpr (F32) {
-    // ---- epilogue, FP32 result: straight from the accumulators ----
-    // Lane owns D[m][n .. n+3] (16 bytes), m = row l%32 of the MFMA tile, n = 8*(r/4) + 4*(l/32);
-    // with accumulate, the old value is read and the sum written back (one owner per element).
+    // ---- epilogue, FP32 result: one 64-row slab at a time through LDS ----
+    // Slab i holds rows wm*WM + 32i + (lane % 32) of both wave rows, staged as row r = wm*32 + lane%32;
+    // each lane writes its 4 consecutive columns per accumulator quarter, then every thread moves
+    // whole 16-byte chunks of whole rows (64 lanes cover a 1 KB row), so the read-modify-write of
+    // the result is coalesced. The old values of a slab are loaded first: their latency overlaps the
+    // staging. Chunk c of staged row r sits at c ^ (r mod FCH): conflict-free writes and reads.
+    constexpr int FCH = BN / 4;                      // 16-byte chunks per FP32 row
+    constexpr int FRP = BN * 4;                      // staged row pitch (bytes)
+    constexpr int FRPB = ST / FRP;                   // staged rows per stage buffer
+    static_assert((FCH & (FCH - 1)) == 0, "FP32 rows are a power-of-two number of chunks");
+    static_assert((64 + FRPB - 1) / FRPB <= NBUF, "a 64-row FP32 slab fits the stage buffers");
+    constexpr int PER_S = 64 * FCH / 256;            // chunks per thread and slab
+    auto fphys = [](int r, int c) -> int { return c ^ (r & (FCH - 1)); };
+    auto srow = [&](int r) -> uint8_t* {
+      return bufs(static_cast<unsigned>(r) / FRPB) + (static_cast<unsigned>(r) % FRPB) * FRP;
+    };
+    // s_waitcnt lgkmcnt(0) only: this wave's LDS accesses are done, stores may stay in flight
+    constexpr int kWaitLgkm = 0xF | (0x7 << 4) | (0x3 << 14);
+    __builtin_amdgcn_s_barrier();  // every wave is done with the operand buffers
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int64_t m = m0 + wm * WM + 32 * i + l32;
+      float4 old[PER_S];
+      if (p.accumulate) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int64_t n = n0 + wn * WN + 32 * j + 8 * q4 + 4 * half;
-          float* dst = p.d32 + m * p.ldd + n;
-          float4 v = make_float4(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
-                                 acc[i][j][4 * q4 + 3]);
-          if (!EDGE || (m < M && n + 3 < N)) {
-            if (p.accumulate) {
-              const float4 o = *reinterpret_cast<const float4*>(dst);
-              v = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
-            }
-            *reinterpret_cast<float4*>(dst) = v;
-          } else if (m < M) {
-            const float w[4] = {v.x, v.y, v.z, v.w};
+        for (int it = 0; it < PER_S; ++it) {
+          const int q = t + 256 * it, r = q / FCH, c = q % FCH;
+          const int64_t gm = m0 + (r >> 5) * WM + 32 * i + (r & 31), gn = n0 + 4 * c;
+          const float* src = p.d32 + gm * p.ldd + gn;
+          if (!EDGE || (gm < M && gn + 3 < N)) {
+            old[it] = *reinterpret_cast<const float4*>(src);
+          } else {
+            float w[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (n + e < N) dst[e] = p.accumulate ? dst[e] + w[e] : w[e];
+              if (gm < M && gn + e < N) w[e] = src[e];
+            old[it] = make_float4(w[0], w[1], w[2], w[3]);
           }
         }
-      // keep the read-modify-write of one 32-row slab in flight at a time (registers)
-      __builtin_amdgcn_sched_barrier(0);
+      }
+      {
+        const int r = wm * 32 + l32;
+        uint8_t* rb = srow(r);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int c = (wn * WN + 32 * j + 8 * q4 + 4 * half) >> 2;
+            *reinterpret_cast<float4*>(rb + fphys(r, c) * 16) =
+                make_float4(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]);
+          }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int it = 0; it < PER_S; ++it) {
+        const int q = t + 256 * it, r = q / FCH, c = q % FCH;
+        const int64_t gm = m0 + (r >> 5) * WM + 32 * i + (r & 31), gn = n0 + 4 * c;
+        float4 v = *reinterpret_cast<const float4*>(srow(r) + fphys(r, c) * 16);
+        if (p.accumulate) v = make_float4(old[it].x + v.x, old[it].y + v.y, old[it].z + v.z, old[it].w + v.w);
+        float* dst = p.d32 + gm * p.ldd + gn;
+        if (!EDGE || (gm < M && gn + 3 < N)) {
+          *reinterpret_cast<float4*>(dst) = v;
+        } else if (gm < M) {
+          const float w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (gn + e < N) dst[e] = w[e];
+        }
+      }
+      // every wave has read this slab back before the next one is staged
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+      __builtin_amdgcn_s_barrier();
     }
     return;
   }
