@@ -24,6 +24,11 @@
  *    sign kept on zero. Inputs must be finite; NaN/Inf inputs give unspecified codes.
  *  - Alignment: every code / bf16 array base is 16-byte aligned, and its row pitch
  *    (ld * element size) is a multiple of 16 bytes. Scale arrays are 4-byte aligned.
+ *  - Row pitches and speed: a GEMM reads (and its epilogue writes) the same column slice of many
+ *    rows at once, and some pitches crowd a few memory channels. Measured on MI355X: code arrays
+ *    whose row pitch is an odd multiple of 4 KiB, and results whose row pitch is any multiple of
+ *    4 KiB, run faster with 128 more bytes of pitch (the Python binding allocates that way).
+ *    Keep every row pitch a multiple of 128 bytes.
  */
 #ifndef PF8_H
 #define PF8_H
