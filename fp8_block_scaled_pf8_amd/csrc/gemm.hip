@@ -722,11 +722,14 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
                                                     (static_cast<unsigned>(row) % RPB) * RP + phys(row, c) * 16);
     const int64_t m = m0 + row, n = n0 + 8 * c;
     uint16_t* dst = p.d + m * p.ldd + n;
+    // non-temporal: the result does not stay in the caches, where the next kernel would pay for its
+    // write-back (in the gate+up layer step: 680.7 -> 656.5 us, the dY quantiser 83.6 -> 70.6 us)
+    const v4i nv = {static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w)};
     if (!EDGE) {
-      *reinterpret_cast<uint4*>(dst) = v;
+      __builtin_nontemporal_store(nv, reinterpret_cast<v4i*>(dst));
     } else if (m < M) {
       if (n + 7 < N) {
-        *reinterpret_cast<uint4*>(dst) = v;
+        __builtin_nontemporal_store(nv, reinterpret_cast<v4i*>(dst));
       } else {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
