@@ -22,7 +22,7 @@ arXiv 2608.27370):
   operands [paperlayer.ai summary, appendix C "Production Training Details",
   bullet "FP8 implementation pipeline"].
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 * block statistic = exact absolute maximum of the current block;
 * scale = smallest power of two 2^e with amax <= 448 * 2^e (never saturates);
