@@ -540,16 +540,23 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   auto prologue = [&](auto h_c) {
     constexpr int H = decltype(h_c)::value;
     // stages 0 .. NST-1, issued in stage order (the explicit waits count loads in that order); of
-    // stage NST-1 only the A-operand part, stage 0 sends the rest like any refill's second part
+    // stage NST-1 only the A-operand part, stage 0 sends the rest like any refill's second part.
+    // A scheduling fence after each stage keeps the compiler from moving one stage's scale loads
+    // among another stage's loads, which would break the counts.
     issue_stage(std::integral_constant<int, (0 - H + NST) % NST>{}, 0);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (NST == 2) issue_part(std::integral_constant<int, (1 - H + NST) % NST>{}, 1, PA{});
     else issue_stage(std::integral_constant<int, (1 - H + NST) % NST>{}, 1);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (NST >= 4) {
       issue_stage(std::integral_constant<int, (2 - H + NST) % NST>{}, 2);
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (NST == 4) issue_part(std::integral_constant<int, (3 - H + NST) % NST>{}, 3, PA{});
       else issue_stage(std::integral_constant<int, (3 - H + NST) % NST>{}, 3);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (NST >= 5) issue_part(std::integral_constant<int, (4 - H + NST) % NST>{}, 4, PA{});
+    __builtin_amdgcn_sched_barrier(0);
     PF8_WAIT_VM_LGKM0(VV * (NST - 2) + VA);
     __builtin_amdgcn_s_barrier();
     constexpr int u0 = (NST - H) % NST;
