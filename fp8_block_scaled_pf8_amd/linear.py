@@ -12,7 +12,8 @@ FP32 weight gradients: given ``main_grad`` (an FP32 [N, K] buffer), the backward
 it in FP32 inside the GEMM's epilogue (pf8_block_gemm_f32 with accumulate = 1), the way gradients
 are summed over the micro-batches of an optimizer step, and autograd receives no gradient for W.
 
-Tokens (the product of the leading dimensions), N and K must be multiples of 128.
+Tokens (the product of the leading dimensions), N and K must be multiples of 128. Zero tokens give
+an empty result and no weight-gradient contribution, without a launch.
 """
 from __future__ import annotations
 
@@ -43,17 +44,26 @@ class Fp8LinearFunction(torch.autograd.Function):
             x2 = x2.contiguous()
         n = w.shape[0]
         _check_shapes(x2.shape[0], n, k)
+        ctx.lead, ctx.k, ctx.main_grad = lead, k, main_grad
+        if x2.shape[0] == 0:
+            # no tokens: an empty result, and no gradient contribution in the backward pass (the
+            # library rejects empty dimensions, so nothing is launched)
+            ctx.empty = True
+            return x.new_empty((*lead, n))
+        ctx.empty = False
         qx, sx, qxt, sxt = ops.quant_act_dual(x2)
         qw, qwt, sw = ops.quant_w_128x128(w.contiguous(), transposed=True)
         # results handed to the caller are plain contiguous tensors (the library's own workspaces
         # use padded row pitches instead)
         y = ops.fprop(qx, sx, qw, sw, out=torch.empty((x2.shape[0], n), dtype=torch.bfloat16, device=x.device))
         ctx.save_for_backward(qxt, sxt, qwt, sw)
-        ctx.lead, ctx.k, ctx.main_grad = lead, k, main_grad
         return y.reshape(*lead, n)
 
     @staticmethod
     def backward(ctx, dy: torch.Tensor):
+        if ctx.empty:
+            dx = dy.new_empty((*ctx.lead, ctx.k), dtype=torch.bfloat16) if ctx.needs_input_grad[0] else None
+            return dx, None, None
         qxt, sxt, qwt, sw = ctx.saved_tensors
         n = qwt.shape[1]
         dy2 = dy.reshape(-1, n)

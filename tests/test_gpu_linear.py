@@ -82,6 +82,22 @@ def test_fp8_linear_rejects_ragged_tokens():
         pf8.fp8_linear(x, w)
 
 
+def test_fp8_linear_empty_batch():
+    """Zero tokens: an empty Y and dX, no weight gradient, the FP32 main gradient left as it was."""
+    w = to_dev_bf16(_bits((256, 384), 41, 0.02, False)).requires_grad_(True)
+    x = torch.empty((0, 7, 384), dtype=torch.bfloat16, device=DEV).requires_grad_(True)
+    y = pf8.fp8_linear(x, w)
+    assert tuple(y.shape) == (0, 7, 256) and y.dtype == torch.bfloat16
+    y.sum().backward()
+    assert tuple(x.grad.shape) == (0, 7, 384) and w.grad is None
+    layer = pf8.Fp8Linear(384, 256, device=DEV, fp32_main_grad=True)
+    layer.weight.main_grad.fill_(1.5)
+    xe = torch.empty((0, 384), dtype=torch.bfloat16, device=DEV, requires_grad=True)
+    layer(xe).sum().backward()
+    torch.cuda.synchronize()
+    assert bool((layer.weight.main_grad == 1.5).all()) and layer.weight.grad is None
+
+
 def test_fp8_linear_noncontiguous_input():
     """A transposed-view input, made contiguous by the layer before quantisation."""
     m, k, n = 256, 384, 128
