@@ -255,3 +255,36 @@ def test_no_device_is_reported_after_validation():
     assert _gm() == L.PF8_ENODEV
     assert L.pf8_block_gemm(L.PF8_WGRAD, 256, 384, 512, A16, 512, S4, 256, B16, 512, S4, 1, 4, C16, 384, 0) == \
         L.PF8_ENODEV
+
+
+def test_size_limits_are_exact():
+    """The largest accepted sizes pass validation (and then find no device here); one step beyond
+    is PF8_ESHAPE. Limits: 65535 grid rows of 128-groups in the quantisers, and a row pitch whose
+    256-row tile offsets fit a signed 32-bit offset in the GEMMs."""
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present (the fake addresses would reach a kernel)")
+    gmax = 65535 * 128
+    pmax = ((1 << 31) - 1) // 256
+    kmax = pmax // 128 * 128
+    # row mode: one grid row per 128-group of a row
+    assert _qa(rows=1, cols=gmax, ldx=gmax, ldq=gmax, ld_s=1) == L.PF8_ENODEV
+    assert _qa(rows=1, cols=gmax + 128, ldx=gmax + 128, ldq=gmax + 128, ld_s=1) == L.PF8_ESHAPE
+    # col mode: one grid row per 128-row band
+    assert _qa(axis=L.PF8_ALONG_ROWS, rows=gmax, cols=8, ldx=8, ldq=gmax, ld_s=8) == L.PF8_ENODEV
+    assert _qa(axis=L.PF8_ALONG_ROWS, rows=gmax + 128, cols=8, ldx=8, ldq=gmax + 128, ld_s=8) == L.PF8_ESHAPE
+    # dual: grid rows are the 128-row bands
+    assert _qd(rows=gmax, cols=128, ldx=128, ldqr=128, ld_sr=gmax, ldqc=gmax, ld_sc=128) == L.PF8_ENODEV
+    assert _qd(rows=gmax + 128, cols=128, ldx=128, ldqr=128, ld_sr=gmax + 128, ldqc=gmax + 128,
+               ld_sc=128) == L.PF8_ESHAPE
+    # weight tiles: one grid row per 128-row tile band
+    assert _qw(n=gmax, k=128, ldw=128, ldq=128, ldqt=gmax, ld_s=1) == L.PF8_ENODEV
+    assert _qw(n=gmax + 128, k=128, ldw=128, ldq=128, ldqt=gmax + 128, ld_s=1) == L.PF8_ESHAPE
+    # GEMM row pitch (FP8 codes: bytes; the BF16 GEMM's pitch is in elements of 2 bytes)
+    assert _gm(m=3, n=2, k=kmax, lda=pmax // 16 * 16, ldb=kmax, ld_as=3, ldd=8, sb_n=kmax // 128) == L.PF8_ENODEV
+    assert _gm(m=3, n=2, k=kmax, lda=pmax // 16 * 16 + 16, ldb=kmax, ld_as=3, ldd=8,
+               sb_n=kmax // 128) == L.PF8_ESHAPE
+    assert _gf(m=3, n=2, k=kmax, lda=kmax, ldb=kmax, ld_as=3, sb_n=1, sb_k=2, ldd=4) == L.PF8_ENODEV
+    assert _gf(m=3, n=2, k=kmax + 128, lda=kmax + 128, ldb=kmax + 128, ld_as=3, sb_n=1, sb_k=2,
+               ldd=4) == L.PF8_ESHAPE
