@@ -303,6 +303,45 @@ def test_linear_step_matches_oracle(fused):
     _report(bf16_f64(step.dw), oracle.gemm_wgrad(qdyt, sdyt, qxt, sxt), "step wgrad")
 
 
+def test_linear_step_on_a_side_stream_and_in_a_graph():
+    """The library enqueues on the caller's stream and allocates nothing, so the step runs on a
+    side stream and replays from a captured HIP graph. Every replay (with eager work in between
+    that overwrites the results) equals the eager default-stream run bit for bit."""
+    t = generate("tiny_fprop")
+    dyb = _rand_bits((256, 384), 43, 1e-3, outliers=False)
+    step = pf8.LinearStep(to_dev_bf16(t["X"]), to_dev_bf16(t["W"]), to_dev_bf16(dyb))
+    outs = lambda: [o.clone() for o in (step.y, step.dx, step.dw, step.qx, step.qdyt, step.sxt)]  # noqa: E731
+    step.run()
+    torch.cuda.synchronize()
+    want = outs()
+    side = torch.cuda.Stream()
+    for o in (step.y, step.dx, step.dw):
+        o.fill_(float("nan"))
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step.run()
+    side.synchronize()
+    for got, ref in zip(outs(), want):
+        assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8))
+    graph = torch.cuda.CUDAGraph()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step.run()  # warm-up on the capturing side stream, as torch asks
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        step.run()
+    for rep in range(3):
+        for o in (step.y, step.dx, step.dw):
+            o.fill_(float("nan"))
+        step.qx.fill_(0)
+        step.sxt.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip(outs(), want):
+            assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), f"replay {rep}"
+
+
 def test_layer_step_workload_sampled():
     """The benchmark's gate+up layer pass at full size: sampled codes and outputs against the oracle.
 
