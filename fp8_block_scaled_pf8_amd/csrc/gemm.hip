@@ -240,6 +240,14 @@ __global__ __launch_bounds__(256) void gemm_promote_kernel(GemmArgs p, int tiles
 // evenly between them (sched_group_barrier masks: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read).
 // Bunching the refill loads behind the last few MFMAs fills the texture unit's queues and stalls
 // the wave's instruction stream, matrix instructions included.
+// Vector-memory operations of `cnt` consecutive stages whose first is odd (`odd`) or even: D
+// direct-to-LDS loads each, plus SS scale loads in each even stage.
+constexpr int stage_ops(int cnt, bool odd, int d, int ss) {
+  int n = 0;
+  for (int i = 0; i < cnt; ++i) n += d + ((odd ? 1 : 0) ^ (i & 1) ? 0 : ss);
+  return n;
+}
+
 template <int NM, int NV, int ND, int X = 0>
 __device__ __forceinline__ void interleave_groups() {
   if constexpr (X < NM) {
@@ -269,12 +277,13 @@ __device__ __forceinline__ void interleave_groups() {
 //    reads the next stage's operands into the other fragment set while the second half of the
 //    MFMAs runs. The refill's A-operand loads go out in that second half, its scales and B-operand
 //    loads in the first half of the next stage, so the texture unit sees a steady stream.
-//  * Stage s lives in buffer (s - h) mod NST with h = (stage count) mod NST, so that the main loop
-//    (unrolled by NST) and the final NST stages always use buffers 0..NST-1 in order; only the first
-//    h stages (a short head, one code path per h) start elsewhere. Every buffer access thereby names
-//    a fixed LDS object and the compiler can track each buffer's direct-to-LDS loads separately.
-//  * The block scales of a stage travel with its operands: they are loaded into the scale registers
-//    of the stage's buffer when the stage is issued, NST stages before use.
+//  * Stage s lives in buffer (s - h) mod NST. With five buffers the main loop runs ten stages
+//    per trip and h = (stage count - 5) mod 10 (a short head, one code path per h), so the loop and
+//    the final five stages always start in buffer 0 on an odd stage. Every buffer access thereby
+//    names a fixed LDS object, and every stage's parity is known at compile time.
+//  * The block scales travel with the operands, one set per 128-wide K block: the even stage of
+//    the block loads them into its buffer's scale registers when it is issued, NST stages before
+//    use, and the odd stage reads the previous buffer's registers.
 // BF16IN: the operands are BF16 instead of E4M3 codes and carry no scales (the plain BF16 GEMM
 // kept for comparison); K, the pitches and the stage size are then counted in bytes, a 64-byte
 // stage is 32 values, and each fragment pair feeds two v_mfma_f32_32x32x16_bf16 (its first and
@@ -286,7 +295,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   constexpr int A_ST = BM * BK, ST = (BM + BN) * BK;
   constexpr int A_DMA = BM / 64, B_DMA = BN / 64, D = A_DMA + B_DMA;  // loads per wave per stage
-  static_assert(NST == 2 || NST == 4 || NST == 5, "two, four or five stage buffers");
+  static_assert(NST == 2 || NST == 5, "two or five stage buffers");
   // at least four buffers: the epilogue stages the BM x BN output tile through them
   constexpr int NBUF = NST < 4 ? 4 : NST;
   __shared__ __align__(16) uint8_t buf0[ST];
@@ -318,7 +327,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   const int tn = __builtin_amdgcn_readfirstlane(in_grp / gsize);
   const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * BN;
   const int64_t M = p.m, N = p.n;
-  const int ns = static_cast<int>(p.k / BK);  // stages (>= NST, checked by the launcher)
+  const int ns = static_cast<int>(p.k / BK);  // stages: even, and >= 6 with five buffers (the launcher checks)
 
   auto bufs = [&](int u) -> uint8_t* {
     return u == 0 ? buf0 : u == 1 ? buf1 : u == 2 ? buf2 : u == 3 ? buf3 : buf4;
@@ -348,14 +357,14 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   // with tile scales and a wave's columns inside one 128-column tile, one B scale serves all j
   constexpr bool B_ONE = !ROW_B && (WN == 128) && !EDGE;
   constexpr int SB = B_ONE ? 1 : TN;
-  // vector-memory operations a wave issues per stage: scale loads and direct-to-LDS loads
-  constexpr int VV = D + (BF16IN ? 0 : TM + SB);
+  // The two stages of a 128-wide K block share one set of scales: the even stage loads it into
+  // its buffer's scale registers, the odd stage reads the previous buffer's. A stage's parity is
+  // known at compile time wherever it is issued or consumed (see the stage layout below), and a
+  // wave issues D direct-to-LDS loads per stage plus SS scale loads in an even stage.
+  constexpr int SS = BF16IN ? 0 : TM + SB;
   uint32_t sc_a[NBUF][TM], sc_b[NBUF][SB];
   auto load_scales = [&](int s, uint32_t (&sa)[TM], uint32_t (&sb)[SB]) {
-    int64_t kb = s >> 1;
-    // the two stages of a K block load the same scales; an opaque block index keeps the second
-    // set of loads from being merged into the first, so every stage issues exactly VV operations
-    asm volatile("" : "+s"(kb));
+    const int64_t kb = s >> 1;
 #pragma unroll
     for (int i = 0; i < TM; ++i) sa[i] = __float_as_uint(p.a_dscale[kb * p.ld_as + a_row[i]]);
 #pragma unroll
@@ -366,12 +375,12 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   };
 
   // Loads of stage s into buffer u: part 0 = the A operand's direct-to-LDS loads, part 1 = the
-  // stage's scales and the B operand's loads, part 2 = all of them.
-  auto issue_part = [&](auto u_c, int s, auto part_c) {
+  // stage's scales (an even stage's) and the B operand's loads, part 2 = all of them.
+  auto issue_part = [&](auto u_c, int s, auto part_c, auto even_c) {
     constexpr int part = decltype(part_c)::value;
     constexpr int u = decltype(u_c)::value;
     uint8_t* buf = bufs(u);
-    if constexpr (!BF16IN && part != 0) load_scales(s, sc_a[u], sc_b[u]);
+    if constexpr (!BF16IN && part != 0 && decltype(even_c)::value) load_scales(s, sc_a[u], sc_b[u]);
     const int kofs = s * BK;
 #pragma unroll
     for (int j = 0; j < (part == 1 ? 0 : A_DMA); ++j) {
@@ -391,9 +400,13 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   using PA = std::integral_constant<int, 0>;
   using PB = std::integral_constant<int, 1>;
   using PALL = std::integral_constant<int, 2>;
-  auto issue_stage = [&](auto u_c, int s) { issue_part(u_c, s, PALL{}); };
-  // vector-memory operations of the two parts of a refill
-  constexpr int VA = A_DMA, VB = VV - A_DMA;
+  // a whole stage in the order a split refill uses (A operand, then scales and B operand), so that
+  // the prologue leaves the loads in flight in the same order as every later stage
+  auto issue_stage = [&](auto u_c, int s, auto even_c) {
+    issue_part(u_c, s, PA{}, even_c);
+    issue_part(u_c, s, PB{}, even_c);
+  };
+  constexpr int VA = A_DMA;  // vector-memory operations of a refill's first part
 
   // ---- operand fragments: set f = (buffer index) & 1 ----
   const int sw = (l32 >> 2) & 3;
@@ -440,24 +453,34 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   // s + NST is split in two to spread the loads over a whole stage of MFMAs: with `refill` the
   // A-operand loads go out in this stage's second half; with `prev` this stage's first half sends
   // the scales and B-operand loads of the previous stage's refill (stage s - 1 + NST).
-  auto stage = [&](int s, auto u_c, bool refill, auto last_c, auto prev_c) {
+  // Stage s is odd (`odd_c`) or even; a stage without `refill_c` has `after_c` stages issued
+  // after stage s+1 (the final stages of K).
+  auto stage = [&](int s, auto u_c, auto refill_c, auto last_c, auto prev_c, auto odd_c, auto after_c) {
     constexpr int u = decltype(u_c)::value;
+    constexpr bool refill = decltype(refill_c)::value;
     constexpr bool prev = decltype(prev_c)::value;
     constexpr bool last = decltype(last_c)::value;
+    constexpr bool odd = decltype(odd_c)::value;
+    constexpr int after = decltype(after_c)::value;
     constexpr int f = u & 1, un = (u + 1) % NST, fn = un & 1;
+    // an odd stage's scales sit in the previous buffer's registers (loaded with the even stage)
+    constexpr int us = odd ? (u + NST - 1) % NST : u;
+    // the previous stage's refill (stage s - 1 + NST) is even when this stage is (NST odd), or when
+    // this stage is odd (NST even)
+    constexpr bool prev_even = (NST % 2 == 1) ? !odd : odd;
     // decode this stage's scales; the empty asm hands each raw value over opaquely so the decode
     // (and the wait for its load, issued NST stages ago) cannot be hoisted next to the load
     int sae[TM], sbe[TN];
     if constexpr (!BF16IN) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        uint32_t v = sc_a[u][i];
+        uint32_t v = sc_a[us][i];
         asm volatile("" : "+v"(v));
         sae[i] = static_cast<int>(v >> 23);
       }
 #pragma unroll
       for (int j = 0; j < SB; ++j) {
-        uint32_t v = sc_b[u][j];
+        uint32_t v = sc_b[us][j];
         asm volatile("" : "+v"(v));
         sbe[j] = static_cast<int>(v >> 23);
       }
@@ -483,31 +506,22 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
       }
     };
     // second part of the previous stage's refill (its buffer is free since the last barrier)
-    if constexpr (prev) issue_part(std::integral_constant<int, (u + NST - 1) % NST>{}, s - 1 + NST, PB{});
+    if constexpr (prev)
+      issue_part(std::integral_constant<int, (u + NST - 1) % NST>{}, s - 1 + NST, PB{},
+                 std::integral_constant<bool, prev_even>{});
     mfma_rows(0, TM / 2);
-    if constexpr (prev) interleave_groups<(TM / 2) * TN * (BF16IN ? 2 : 1), VB, 0>();  // loads between the MFMAs
+    if constexpr (prev)  // loads between the MFMAs
+      interleave_groups<(TM / 2) * TN * (BF16IN ? 2 : 1), B_DMA + (prev_even ? SS : 0), 0>();
     // the first half of the MFMAs stays ahead of the wait and barrier: it keeps the matrix core
     // busy while the waves line up
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (!last) {
-      // stages s+2 .. s+NST-1 (VV operations each) may still be in flight (fewer near the end of K)
-      if (refill) {
-        PF8_WAIT_VM_LGKM0(VV * (NST - 2));
-      } else {
-        const int after = ns - 2 - s;  // stages issued after stage s+1
-        if constexpr (NST >= 5) {
-          if (after >= 3) PF8_WAIT_VM_LGKM0(VV * 3);
-          else if (after == 2) PF8_WAIT_VM_LGKM0(VV * 2);
-          else if (after == 1) PF8_WAIT_VM_LGKM0(VV);
-          else PF8_WAIT_VM_LGKM0(0);
-        } else {
-          if (after >= 2) PF8_WAIT_VM_LGKM0(VV * 2);
-          else if (after == 1) PF8_WAIT_VM_LGKM0(VV);
-          else PF8_WAIT_VM_LGKM0(0);
-        }
-      }
+      // stages s+2 .. s+NST-1 may still be in flight (fewer near the end of K); stage s+2 has
+      // this stage's parity
+      constexpr int inflight = refill ? NST - 2 : (after < NST - 2 ? after : NST - 2);
+      PF8_WAIT_VM_LGKM0(stage_ops(inflight, odd, D, SS));
       __builtin_amdgcn_s_barrier();
-      if (refill) issue_part(u_c, s + NST, PA{});
+      if constexpr (refill) issue_part(u_c, s + NST, PA{}, std::false_type{});
       if constexpr (fn != f) read_frags(bufs(un), fa[fn], fb[fn]);
       else read_frags_a(bufs(un), fa[fn], 0, TM / 2);  // only A rows the first half no longer needs
     }
@@ -529,90 +543,101 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  using I4 = std::integral_constant<int, 4>;
   using F = std::false_type;
   using T = std::true_type;
-  auto uc = [](auto x) { return x; };
-  (void)uc;
-
-  // ---- prologue and head: stage s lives in buffer (s - h) mod NST ----
-  const int h = ns % NST;
+  // Stage layout. K has ns stages, and ns is even: a multiple of 128 FP8 values, or of 128 BF16
+  // values in the BF16 kernel. With five buffers the main loop runs ten stages per trip, so every
+  // stage's buffer and parity are compile-time constants of its position in the loop body. The
+  // first h = (ns - 5) mod 10 stages (h odd) form the head, one code path per h, and the last five
+  // form the tail. Stage s lives in buffer (s - h) mod 5, so the loop and the tail always start in
+  // buffer 0 on an odd stage. With two buffers there is no head: stage s lives in buffer s mod 2,
+  // which is also its parity.
+  const int h = NST == 5 ? static_cast<int>((ns - 5) % 10) : 0;
   auto prologue = [&](auto h_c) {
     constexpr int H = decltype(h_c)::value;
+    auto ub = [](auto k_c) { return std::integral_constant<int, ((decltype(k_c)::value - H) % NST + NST) % NST>{}; };
     // stages 0 .. NST-1, issued in stage order (the explicit waits count loads in that order); of
     // stage NST-1 only the A-operand part, stage 0 sends the rest like any refill's second part.
     // A scheduling fence after each stage keeps the compiler from moving one stage's scale loads
     // among another stage's loads, which would break the counts.
-    issue_stage(std::integral_constant<int, (0 - H + NST) % NST>{}, 0);
+    issue_stage(ub(I0{}), 0, T{});
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NST == 2) issue_part(std::integral_constant<int, (1 - H + NST) % NST>{}, 1, PA{});
-    else issue_stage(std::integral_constant<int, (1 - H + NST) % NST>{}, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NST >= 4) {
-      issue_stage(std::integral_constant<int, (2 - H + NST) % NST>{}, 2);
+    if constexpr (NST == 2) {
+      issue_part(ub(I1{}), 1, PA{}, F{});
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (NST == 4) issue_part(std::integral_constant<int, (3 - H + NST) % NST>{}, 3, PA{});
-      else issue_stage(std::integral_constant<int, (3 - H + NST) % NST>{}, 3);
+      PF8_WAIT_VM_LGKM0(VA);
+    } else {
+      issue_stage(ub(I1{}), 1, F{});
       __builtin_amdgcn_sched_barrier(0);
+      issue_stage(ub(I2{}), 2, T{});
+      __builtin_amdgcn_sched_barrier(0);
+      issue_stage(ub(I3{}), 3, F{});
+      __builtin_amdgcn_sched_barrier(0);
+      issue_part(ub(std::integral_constant<int, 4>{}), 4, PA{}, T{});
+      __builtin_amdgcn_sched_barrier(0);
+      PF8_WAIT_VM_LGKM0(stage_ops(3, true, D, SS) + VA);  // after stage 0: stages 1..3 and stage 4's A part
     }
-    if constexpr (NST >= 5) issue_part(std::integral_constant<int, (4 - H + NST) % NST>{}, 4, PA{});
-    __builtin_amdgcn_sched_barrier(0);
-    PF8_WAIT_VM_LGKM0(VV * (NST - 2) + VA);
     __builtin_amdgcn_s_barrier();
-    constexpr int u0 = (NST - H) % NST;
+    constexpr int u0 = decltype(ub(I0{}))::value;
     read_frags(bufs(u0), fa[u0 & 1], fb[u0 & 1]);
-    // head stages 0 .. H-1 in buffers NST-H .. NST-1 (all refill: ns >= NST + H)
-    if constexpr (H >= 1) stage(0, std::integral_constant<int, NST - H>{}, true, F{}, T{});
-    if constexpr (H >= 2) stage(1, std::integral_constant<int, NST - H + 1>{}, true, F{}, T{});
-    if constexpr (H >= 3) stage(2, std::integral_constant<int, NST - H + 2>{}, true, F{}, T{});
-    if constexpr (H >= 4) stage(3, std::integral_constant<int, NST - H + 3>{}, true, F{}, T{});
+    // head stages 0 .. H-1 (all refill: ns >= H + 5)
+    auto head = [&](auto j_c) {
+      constexpr int J = decltype(j_c)::value;
+      if constexpr (J < H) stage(J, ub(j_c), T{}, F{}, T{}, std::integral_constant<bool, (J & 1) != 0>{}, I0{});
+    };
+    head(I0{});
+    head(I1{});
+    head(I2{});
+    head(I3{});
+    head(std::integral_constant<int, 4>{});
+    head(std::integral_constant<int, 5>{});
+    head(std::integral_constant<int, 6>{});
+    head(std::integral_constant<int, 7>{});
+    head(std::integral_constant<int, 8>{});
   };
   if constexpr (NST == 5) {
     switch (h) {
-      case 0: prologue(I0{}); break;
       case 1: prologue(I1{}); break;
-      case 2: prologue(I2{}); break;
       case 3: prologue(I3{}); break;
-      default: prologue(I4{}); break;
-    }
-  } else if constexpr (NST == 4) {
-    switch (h) {
-      case 0: prologue(I0{}); break;
-      case 1: prologue(I1{}); break;
-      case 2: prologue(I2{}); break;
-      default: prologue(I3{}); break;
+      case 5: prologue(std::integral_constant<int, 5>{}); break;
+      case 7: prologue(std::integral_constant<int, 7>{}); break;
+      default: prologue(std::integral_constant<int, 9>{}); break;
     }
   } else {
-    if (h == 0) prologue(I0{});
-    else prologue(I1{});
+    prologue(I0{});
   }
 
-  // ---- main loop: NST stages per trip, buffers 0 .. NST-1 ----
+  // ---- main loop and tail ----
+  using OD = std::true_type;   // odd stage
+  using EV = std::false_type;  // even stage
+  auto U = [](auto k_c) { return std::integral_constant<int, decltype(k_c)::value % NST>{}; };
   int s = h;
-  for (; s < ns - NST; s += NST) {
-    stage(s, I0{}, true, F{}, T{});
-    stage(s + 1, I1{}, true, F{}, T{});
-    if constexpr (NST >= 4) {
-      stage(s + 2, I2{}, true, F{}, T{});
-      stage(s + 3, I3{}, true, F{}, T{});
-    }
-    if constexpr (NST >= 5) stage(s + 4, I4{}, true, F{}, T{});
-  }
-  // ---- last NST stages: nothing left to fetch ----
   if constexpr (NST == 5) {
-    stage(s, I0{}, false, F{}, T{});
-    stage(s + 1, I1{}, false, F{}, F{});
-    stage(s + 2, I2{}, false, F{}, F{});
-    stage(s + 3, I3{}, false, F{}, F{});
-    stage(s + 4, I4{}, false, T{}, F{});
-  } else if constexpr (NST == 4) {
-    stage(s, I0{}, false, F{}, T{});
-    stage(s + 1, I1{}, false, F{}, F{});
-    stage(s + 2, I2{}, false, F{}, F{});
-    stage(s + 3, I3{}, false, T{}, F{});
+    for (; s < ns - 5; s += 10) {
+      stage(s, U(I0{}), T{}, F{}, T{}, OD{}, I0{});
+      stage(s + 1, U(I1{}), T{}, F{}, T{}, EV{}, I0{});
+      stage(s + 2, U(I2{}), T{}, F{}, T{}, OD{}, I0{});
+      stage(s + 3, U(I3{}), T{}, F{}, T{}, EV{}, I0{});
+      stage(s + 4, U(std::integral_constant<int, 4>{}), T{}, F{}, T{}, OD{}, I0{});
+      stage(s + 5, U(std::integral_constant<int, 5>{}), T{}, F{}, T{}, EV{}, I0{});
+      stage(s + 6, U(std::integral_constant<int, 6>{}), T{}, F{}, T{}, OD{}, I0{});
+      stage(s + 7, U(std::integral_constant<int, 7>{}), T{}, F{}, T{}, EV{}, I0{});
+      stage(s + 8, U(std::integral_constant<int, 8>{}), T{}, F{}, T{}, OD{}, I0{});
+      stage(s + 9, U(std::integral_constant<int, 9>{}), T{}, F{}, T{}, EV{}, I0{});
+    }
+    // last five stages: nothing left to fetch
+    stage(s, I0{}, F{}, F{}, T{}, OD{}, I3{});
+    stage(s + 1, I1{}, F{}, F{}, F{}, EV{}, I2{});
+    stage(s + 2, I2{}, F{}, F{}, F{}, OD{}, I1{});
+    stage(s + 3, I3{}, F{}, F{}, F{}, EV{}, I0{});
+    stage(s + 4, std::integral_constant<int, 4>{}, F{}, T{}, F{}, OD{}, I0{});
   } else {
-    stage(s, I0{}, false, F{}, T{});
-    stage(s + 1, I1{}, false, T{}, F{});
+    for (; s < ns - 2; s += 2) {
+      stage(s, I0{}, T{}, F{}, T{}, EV{}, I0{});
+      stage(s + 1, I1{}, T{}, F{}, T{}, OD{}, I0{});
+    }
+    stage(s, I0{}, F{}, F{}, T{}, EV{}, I0{});
+    stage(s + 1, I1{}, F{}, T{}, F{}, OD{}, I0{});
   }
 #undef PF8_WAIT_VM_LGKM0
 
@@ -758,6 +783,7 @@ static hipError_t launch_tile(const GemmArgs& args, hipStream_t stream) {
     // stages take the two-buffer pipeline
     static_assert(5 * (BM + BN) * 64 <= 160 * 1024, "five stage buffers fit the LDS");
     const int64_t ns = args.k / 64;
+    if (ns < 2 || ns % 2 != 0) return hipErrorInvalidValue;  // the stage layout needs whole K blocks
     // FP32 results (three tile shapes only): one edge-checked kernel per pipeline depth
     constexpr bool kF32Tile = (BM == 256 && BN == 256) || (BM == 192 && BN == 256) || (BM == 128 && BN == 128);
     if (args.d32 != nullptr) {
@@ -797,6 +823,7 @@ static hipError_t launch_bf16_tile(const GemmArgs& args, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n)), block(256);
   const bool edge = args.m % BM != 0 || args.n % BN != 0;
   const int64_t ns = args.k / 64;
+  if (ns < 2 || ns % 2 != 0) return hipErrorInvalidValue;  // the stage layout needs an even stage count
   if (edge) {
     if (ns >= 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false, true, 5, false, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
     else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false, true, 2, false, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
