@@ -354,8 +354,10 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   for (int i = 0; i < TM; ++i) a_row[i] = EDGE ? min64(m0 + wm * WM + 32 * i + l32, M - 1) : m0 + wm * WM + 32 * i + l32;
 #pragma unroll
   for (int j = 0; j < TN; ++j) b_row[j] = EDGE ? min64(n0 + wn * WN + 32 * j + l32, N - 1) : n0 + wn * WN + 32 * j + l32;
-  // with tile scales and a wave's columns inside one 128-column tile, one B scale serves all j
-  constexpr bool B_ONE = !ROW_B && (WN == 128) && !EDGE;
+  // With tile scales and WN dividing 128, a wave's columns lie in one 128-column tile, and one B
+  // scale serves all j. In an edge tile the columns clamp to N-1, which is in that tile whenever
+  // any of them is stored.
+  constexpr bool B_ONE = !ROW_B && (128 % WN == 0);
   constexpr int SB = B_ONE ? 1 : TN;
   // The two stages of a 128-wide K block share one set of scales: the even stage loads it into
   // its buffer's scale registers, the odd stage reads the previous buffer's. A stage's parity is
@@ -364,12 +366,21 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   constexpr int SS = BF16IN ? 0 : TM + SB;
   uint32_t sc_a[NBUF][TM], sc_b[NBUF][SB];
   auto load_scales = [&](int s, uint32_t (&sa)[TM], uint32_t (&sb)[SB]) {
+    // The explicit vmcnt counts assume that exactly TM + SB loads go out here, in program order
+    // with the direct-to-LDS loads around them. Every index therefore passes through an opaque
+    // asm statement: the compiler can neither merge two loads whose addresses it proves equal
+    // (known bits of clamped columns let it do so) nor hoist one above earlier loads.
     const int64_t kb = s >> 1;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sa[i] = __float_as_uint(p.a_dscale[kb * p.ld_as + a_row[i]]);
+    for (int i = 0; i < TM; ++i) {
+      int64_t idx = kb * p.ld_as + a_row[i];
+      asm volatile("" : "+v"(idx));
+      sa[i] = __float_as_uint(p.a_dscale[idx]);
+    }
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
-      const int64_t idx = ROW_B ? kb * p.sb_k + b_row[j] * p.sb_n : (b_row[j] >> 7) * p.sb_n + kb * p.sb_k;
+      int64_t idx = ROW_B ? kb * p.sb_k + b_row[j] * p.sb_n : (b_row[j] >> 7) * p.sb_n + kb * p.sb_k;
+      asm volatile("" : "+v"(idx));
       sb[j] = __float_as_uint(p.b_dscale[idx]);
     }
   };

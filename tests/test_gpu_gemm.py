@@ -408,6 +408,34 @@ def test_gemm_f32_matches_oracle_and_bf16_path(lname, m, n, k):
     assert np.array_equal(oracle.bf16_round_from_f64(got), bf16_bits(d16))
 
 
+@pytest.mark.parametrize("lname", ["fprop", "dgrad"])
+def test_gemm_many_rounds_matches_f32_path_and_oracle(lname):
+    """A launch of four rounds of 256x256 tiles on 256 CUs (16 x 64 = 1024 tiles, K = 384): every
+    output must equal the rounded result of the FP32 kernel, and sampled rows (the first and last
+    included) must meet the oracle's tolerance."""
+    layout = LAYOUTS[lname]
+    m, n, k = 4096, 16384, 384
+    if layout == pf8.PF8_FPROP:
+        qa, sa = oracle.quant_act_1x128(_rand_bits((m, k), 91), "cols")
+        qb, _, sb = oracle.quant_w_128x128(_rand_bits((n, k), 92, 0.02, outliers=False))
+        sb_n, sb_k = sb.shape[1], 1
+        ref_rows = lambda r: oracle.gemm_fprop(qa[r], sa[:, r], qb, sb)  # noqa: E731
+    else:
+        qa, sa = oracle.quant_act_1x128(_rand_bits((m, k), 93, 1e-3, outliers=False), "cols")
+        _, qb, sb = oracle.quant_w_128x128(_rand_bits((k, n), 94, 0.01, outliers=False))
+        sb_n, sb_k = 1, sb.shape[1]
+        ref_rows = lambda r: oracle.gemm_dgrad(qa[r], sa[:, r], qb, sb)  # noqa: E731
+    a, sa_d, b, sb_d = to_dev_u8(qa), to_dev_f32(sa), to_dev_u8(qb), to_dev_f32(sb)
+    d16 = pf8.block_gemm(layout, a, sa_d, b, sb_d, sb_n, sb_k)
+    d32 = pf8.block_gemm_f32(layout, a, sa_d, b, sb_d, sb_n, sb_k)
+    torch.cuda.synchronize()
+    assert torch.equal(d32.to(torch.bfloat16).view(torch.int16), d16.view(torch.int16))
+    rows = np.concatenate([[0], np.sort(np.random.default_rng(95).choice(m - 2, 62, replace=False) + 1), [m - 1]])
+    got = bf16_f64(d16[torch.from_numpy(rows).to(DEV)])
+    rep = oracle.gemm_tolerance_report(got, ref_rows(rows))
+    assert rep["violations"] == 0, f"{lname}: {rep}"
+
+
 @pytest.mark.parametrize("lname", ["wgrad", "fprop"])
 def test_gemm_f32_accumulates_into_output(lname):
     layout = LAYOUTS[lname]
