@@ -436,6 +436,56 @@ def test_gemm_many_rounds_matches_f32_path_and_oracle(lname):
     assert rep["violations"] == 0, f"{lname}: {rep}"
 
 
+# One ragged (M, N) per macro-tile the launcher picks (128x128, 256x128, 256x192, 192x256,
+# 256x256), and K values whose stage counts (K/64 = 8, 12, 14) give the K loop's head lengths
+# 3, 7 and 9 (the shapes above cover 1 and 5, and the two-buffer pipeline).
+HEAD_TILES = [(300, 200), (644, 5407), (1421, 5407), (2050, 5407), (2309, 4874)]
+
+
+def _codes(rng, shape):
+    q = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0  # no NaN codes
+    return q
+
+
+@pytest.mark.parametrize("lname", list(LAYOUTS))
+@pytest.mark.parametrize("k", [512, 768, 896])
+@pytest.mark.parametrize("mn", HEAD_TILES, ids=lambda t: f"{t[0]}x{t[1]}")
+def test_every_tile_shape_and_head_length(mn, k, lname):
+    """Random E4M3 codes (every finite code, so both operands are heavy-tailed) with power-of-two
+    scales per block; sampled output rows (first and last included) against the oracle, within
+    the workloads' bar plus the FP8 MFMA's chunk allowance 2^-11 * sum|a*b| (as in
+    test_heavy_tailed_operands_within_chunk_bound)."""
+    m, n = mn
+    layout = LAYOUTS[lname]
+    rng = np.random.default_rng(m * 31 + n * 7 + k + layout)
+    qa, qb = _codes(rng, (m, k)), _codes(rng, (n, k))
+    pow2 = lambda *sh: np.ldexp(1.0, rng.integers(-6, 7, size=sh)).astype(np.float32)  # noqa: E731
+    sa = pow2(k // 128, m)
+    nt = (n + 127) // 128
+    if layout == pf8.PF8_FPROP:
+        sb, sb_n, sb_k = pow2(nt, k // 128), k // 128, 1
+        ref_rows = lambda r: oracle.gemm_fprop(qa[r], sa[:, r], qb, sb)  # noqa: E731
+        deq_b = oracle.dequant_w_tiles(qb, sb)
+    elif layout == pf8.PF8_DGRAD:
+        sb, sb_n, sb_k = pow2(k // 128, nt), 1, nt  # W's tile grid read with swapped strides
+        ref_rows = lambda r: oracle.gemm_dgrad(qa[r], sa[:, r], qb, sb)  # noqa: E731
+        deq_b = oracle.dequant_w_tiles(qb, sb.T)
+    else:
+        sb, sb_n, sb_k = pow2(k // 128, n), 1, n
+        ref_rows = lambda r: oracle.gemm_wgrad(qa[r], sa[:, r], qb, sb)  # noqa: E731
+        deq_b = oracle.dequant_act_groups(qb, sb)
+    d = pf8.block_gemm(layout, to_dev_u8(qa), to_dev_f32(sa), to_dev_u8(qb), to_dev_f32(sb), sb_n, sb_k)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, m - 1], np.random.default_rng(k).choice(m, min(m, 48), replace=False)]))
+    got = bf16_f64(d[torch.from_numpy(rows).to(DEV)])
+    ref = ref_rows(rows)
+    abs_sum = np.abs(oracle.dequant_act_groups(qa[rows], sa[:, rows])) @ np.abs(deq_b).T
+    bound = 2.0 ** -7 * np.abs(ref) + 1e-3 * float(np.sqrt(np.mean(ref * ref))) + 2.0 ** -11 * abs_sum
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), f"{lname} {m}x{n}x{k}: max err/bound {np.max(err / bound):.3f}"
+
+
 @pytest.mark.parametrize("lname", ["wgrad", "fprop"])
 def test_gemm_f32_accumulates_into_output(lname):
     layout = LAYOUTS[lname]
