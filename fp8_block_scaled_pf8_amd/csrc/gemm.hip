@@ -386,7 +386,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   };
 
   // Loads of stage s into buffer u: part 0 = the A operand's direct-to-LDS loads, part 1 = the
-  // stage's scales (an even stage's) and the B operand's loads, part 2 = all of them.
+  // stage's scales (an even stage's) and the B operand's loads.
   auto issue_part = [&](auto u_c, int s, auto part_c, auto even_c) {
     constexpr int part = decltype(part_c)::value;
     constexpr int u = decltype(u_c)::value;
@@ -410,7 +410,6 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   };
   using PA = std::integral_constant<int, 0>;
   using PB = std::integral_constant<int, 1>;
-  using PALL = std::integral_constant<int, 2>;
   // a whole stage in the order a split refill uses (A operand, then scales and B operand), so that
   // the prologue leaves the loads in flight in the same order as every later stage
   auto issue_stage = [&](auto u_c, int s, auto even_c) {
