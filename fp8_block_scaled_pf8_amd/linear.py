@@ -12,12 +12,17 @@ FP32 weight gradients: given ``main_grad`` (an FP32 [N, K] buffer), the backward
 it in FP32 inside the GEMM's epilogue (pf8_block_gemm_f32 with accumulate = 1), the way gradients
 are summed over the micro-batches of an optimizer step, and autograd receives no gradient for W.
 
+Weight codes: W changes only at an optimizer step, so ``Fp8Linear`` quantises it once per weight
+version (codes, transposed codes and tile scales) and reuses them for every micro-batch until W is
+modified. An in-place update of the parameter (as optimizers do) bumps its version counter. An
+update through ``weight.data`` bypasses that counter; call ``invalidate_weight_codes()`` after one.
+
 Tokens (the product of the leading dimensions), N and K must be multiples of 128. Zero tokens give
 an empty result and no weight-gradient contribution, without a launch.
 """
 from __future__ import annotations
 
-from typing import Optional
+from typing import Optional, Tuple
 
 import torch
 
@@ -36,7 +41,8 @@ class Fp8LinearFunction(torch.autograd.Function):
     """Autograd function of the FP8 linear layer (see the module docstring)."""
 
     @staticmethod
-    def forward(ctx, x: torch.Tensor, w: torch.Tensor, main_grad: Optional[torch.Tensor] = None):
+    def forward(ctx, x: torch.Tensor, w: torch.Tensor, main_grad: Optional[torch.Tensor] = None,
+                w_codes: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
         lead = x.shape[:-1]
         k = x.shape[-1]
         x2 = x.reshape(-1, k)
@@ -52,7 +58,7 @@ class Fp8LinearFunction(torch.autograd.Function):
             return x.new_empty((*lead, n))
         ctx.empty = False
         qx, sx, qxt, sxt = ops.quant_act_dual(x2)
-        qw, qwt, sw = ops.quant_w_128x128(w.contiguous(), transposed=True)
+        qw, qwt, sw = w_codes if w_codes is not None else ops.quant_w_128x128(w.contiguous(), transposed=True)
         # results handed to the caller are plain contiguous tensors (the library's own workspaces
         # use padded row pitches instead)
         y = ops.fprop(qx, sx, qw, sw, out=torch.empty((x2.shape[0], n), dtype=torch.bfloat16, device=x.device))
@@ -63,7 +69,7 @@ class Fp8LinearFunction(torch.autograd.Function):
     def backward(ctx, dy: torch.Tensor):
         if ctx.empty:
             dx = dy.new_empty((*ctx.lead, ctx.k), dtype=torch.bfloat16) if ctx.needs_input_grad[0] else None
-            return dx, None, None
+            return dx, None, None, None
         qxt, sxt, qwt, sw = ctx.saved_tensors
         n = qwt.shape[1]
         dy2 = dy.reshape(-1, n)
@@ -80,20 +86,29 @@ class Fp8LinearFunction(torch.autograd.Function):
             ops.wgrad_f32(qdyt, sdyt, qxt, sxt, out=ctx.main_grad, accumulate=True)
         elif ctx.needs_input_grad[1]:
             dw = ops.wgrad(qdyt, sdyt, qxt, sxt, out=torch.empty((n, ctx.k), dtype=torch.bfloat16, device=dy2.device))
-        return dx, dw, None
+        return dx, dw, None, None
 
 
-def fp8_linear(x: torch.Tensor, w: torch.Tensor, main_grad: Optional[torch.Tensor] = None) -> torch.Tensor:
+def fp8_linear(x: torch.Tensor, w: torch.Tensor, main_grad: Optional[torch.Tensor] = None,
+               w_codes: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None) -> torch.Tensor:
     """Y = X . W^T through libpf8's block-scaled FP8 path, differentiable in X and W.
 
     Without ``main_grad`` W's gradient is returned to autograd in BF16. With it (FP32, W's shape,
-    16-byte row pitch) the backward pass adds dW to ``main_grad`` in FP32 instead.
+    16-byte row pitch) the backward pass adds dW to ``main_grad`` in FP32 instead. ``w_codes``
+    are W's codes, transposed codes and tile scales from ``ops.quant_w_128x128(w, transposed=True)``
+    for the current W; without them W is quantised here.
     """
     if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
         raise TypeError("fp8_linear takes bfloat16 X and W")
     if main_grad is not None and (main_grad.dtype != torch.float32 or tuple(main_grad.shape) != tuple(w.shape)):
         raise ValueError("main_grad must be a float32 tensor of W's shape")
-    return Fp8LinearFunction.apply(x, w, main_grad)
+    if w_codes is not None:
+        n, k = w.shape
+        qw, qwt, sw = w_codes
+        if (tuple(qw.shape) != (n, k) or tuple(qwt.shape) != (k, n) or tuple(sw.shape) != (n // GROUP, k // GROUP)
+                or qw.dtype != torch.uint8 or qwt.dtype != torch.uint8 or sw.dtype != torch.float32):
+            raise ValueError("w_codes must be (codes [N,K] uint8, transposed codes [K,N] uint8, scales [N/128,K/128] float32)")
+    return Fp8LinearFunction.apply(x, w, main_grad, w_codes)
 
 
 class Fp8Linear(torch.nn.Module):
@@ -101,6 +116,8 @@ class Fp8Linear(torch.nn.Module):
 
     With ``fp32_main_grad`` the weight carries an FP32 ``main_grad`` buffer that every backward
     pass accumulates into (zero it once per optimizer step); ``weight.grad`` then stays None.
+    The weight's codes are made once per weight version and shared by the micro-batches (see the
+    module docstring).
     """
 
     def __init__(self, in_features: int, out_features: int, device=None, fp32_main_grad: bool = False,
@@ -112,6 +129,23 @@ class Fp8Linear(torch.nn.Module):
         self.weight = torch.nn.Parameter(weight)
         if fp32_main_grad:
             self.weight.main_grad = torch.zeros(self.weight.shape, dtype=torch.float32, device=self.weight.device)
+        self._codes = None
+        self._codes_key = None
+
+    def weight_codes(self) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        """W's codes, transposed codes and tile scales, made once per version of the weight."""
+        w = self.weight
+        key = (w.data_ptr(), w._version, tuple(w.shape), w.device)
+        if self._codes is None or self._codes_key != key:
+            with torch.no_grad():
+                self._codes = ops.quant_w_128x128(w.detach().contiguous(), transposed=True)
+            self._codes_key = key
+        return self._codes
+
+    def invalidate_weight_codes(self) -> None:
+        """Forget the cached weight codes (after a change to W that its version counter misses)."""
+        self._codes = None
+        self._codes_key = None
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
-        return fp8_linear(x, self.weight, getattr(self.weight, "main_grad", None))
+        return fp8_linear(x, self.weight, getattr(self.weight, "main_grad", None), self.weight_codes())

@@ -115,3 +115,37 @@ def test_fp8_linear_noncontiguous_input():
     _check(bf16_f64(y.detach()), ry, "Y")
     _check(bf16_f64(x.grad.contiguous()), rdx, "dX")
     _check(bf16_f64(w.grad), rdw, "dW")
+
+
+def test_fp8_linear_weight_codes_follow_the_weight():
+    """Fp8Linear quantises W once per version: micro-batches share the codes, an optimizer step (an
+    in-place update) makes new ones, and so does invalidate_weight_codes() after a .data write.
+    Each forward is checked against the oracle on the weight as it then stands."""
+    m, k, n = 256, 384, 256
+    layer = pf8.Fp8Linear(k, n, device=DEV, weight=to_dev_bf16(_bits((n, k), 51, 0.02, False)))
+    opt = torch.optim.SGD(layer.parameters(), lr=0.5)
+    xb = _bits((m, k), 52, 1.0, True)
+    dyb = _bits((m, n), 53, 1e-3, False)
+
+    def forward_checked(what):
+        x = to_dev_bf16(xb).requires_grad_(True)
+        y = layer(x)
+        torch.cuda.synchronize()
+        wb = layer.weight.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+        ry = _oracle_layer(xb, wb, dyb)[0]
+        _check(bf16_f64(y.detach()), ry, what)
+        return y
+
+    y = forward_checked("Y, first micro-batch")
+    codes = layer.weight_codes()
+    y.backward(to_dev_bf16(dyb))
+    forward_checked("Y, second micro-batch")
+    assert layer.weight_codes() is codes  # unchanged W: the same codes
+    opt.step()
+    forward_checked("Y after an optimizer step")
+    assert layer.weight_codes() is not codes
+    codes = layer.weight_codes()
+    layer.weight.data.mul_(0.25)  # invisible to the version counter
+    layer.invalidate_weight_codes()
+    forward_checked("Y after a .data write and invalidate_weight_codes()")
+    assert layer.weight_codes() is not codes

@@ -28,3 +28,25 @@ def test_out_pitch():
         for cols in range(1, 9000, 7):
             p = ops.out_pitch(cols, eb)
             assert p >= cols and (p * eb) % 16 == 0 and (p * eb) % 4096 != 0
+
+
+def test_fp8_linear_checks_weight_codes_before_any_launch():
+    """Weight codes of the wrong shape or type are refused on the host."""
+    import pytest
+    import torch
+    from fp8_block_scaled_pf8_amd.linear import fp8_linear
+
+    n, k = 256, 384
+    x = torch.zeros((128, k), dtype=torch.bfloat16)
+    w = torch.zeros((n, k), dtype=torch.bfloat16)
+    good = (torch.zeros((n, k), dtype=torch.uint8), torch.zeros((k, n), dtype=torch.uint8),
+            torch.zeros((n // 128, k // 128), dtype=torch.float32))
+    bad = [
+        (good[0], good[0], good[2]),                                   # codes where the transpose goes
+        (good[0], good[1], torch.zeros((k // 128, n // 128))),         # scale grid transposed
+        (good[0].float(), good[1], good[2]),                           # not uint8
+        (good[0], good[1], good[2].half()),                            # scales not float32
+    ]
+    for codes in bad:
+        with pytest.raises(ValueError, match="w_codes"):
+            fp8_linear(x, w, None, codes)
