@@ -39,6 +39,36 @@ def _check_2d(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
         raise ValueError(f"{name} must have a contiguous last dimension")
 
 
+def _span(t: torch.Tensor) -> int:
+    """Elements from t's first element to the end of its storage."""
+    return t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+
+
+def _check_scales(layout: int, m: int, n: int, k: int, a_dscale: torch.Tensor, b_dscale: torch.Tensor,
+                  sb_n: int, sb_k: int) -> None:
+    """Raise unless every scale a block-scaled GEMM reads lies inside a_dscale and b_dscale.
+
+    The C ABI receives bare pointers and strides and cannot check this; a scale tensor too small
+    for its strides would be read out of bounds on the device. a_dscale is [K/128, >= M].
+    b_dscale is read at (j/128)*sb_n + kb*sb_k (FPROP, DGRAD) or kb*sb_k + j*sb_n (WGRAD) for
+    rows j < N of B and K blocks kb < K/128.
+    """
+    if k <= 0 or k % GROUP or m <= 0 or n <= 0:
+        return  # the C ABI rejects these shapes itself
+    kb = k // GROUP
+    if a_dscale.dim() != 2 or a_dscale.shape[0] < kb or a_dscale.shape[1] < m:
+        raise ValueError(f"a_dscale must cover [K/128, M] = [{kb}, {m}], got {tuple(a_dscale.shape)}")
+    if sb_n < 1 or sb_k < 1:
+        raise ValueError("sb_n and sb_k must be positive")
+    if layout == L.PF8_WGRAD:
+        last = (kb - 1) * sb_k + (n - 1) * sb_n
+    else:
+        last = ((n + GROUP - 1) // GROUP - 1) * sb_n + (kb - 1) * sb_k
+    if last >= _span(b_dscale):
+        raise ValueError(f"b_dscale holds {_span(b_dscale)} scales from its first element, but strides "
+                         f"({sb_n}, {sb_k}) reach element {last}")
+
+
 def code_pitch(cols: int) -> int:
     """Row pitch (bytes) of a buffer of E4M3 codes with `cols` per row. An odd multiple of 4 KiB gets
     128 more bytes. The GEMM reads the same 64-byte column slice of many rows at once, and with such
@@ -135,6 +165,7 @@ def block_gemm(layout: int, a: torch.Tensor, a_dscale: torch.Tensor, b: torch.Te
     n = b.shape[0]
     if b.shape[1] != k:
         raise ValueError(f"reduction dims differ: a {tuple(a.shape)}, b {tuple(b.shape)}")
+    _check_scales(layout, m, n, k, a_dscale, b_dscale, sb_n, sb_k)
     if out is None:
         # the C ABI wants 16-byte row pitches: pad the allocation, hand back the [m, n] view
         out = result_buffer(m, n, torch.bfloat16, a.device)
@@ -163,6 +194,7 @@ def block_gemm_f32(layout: int, a: torch.Tensor, a_dscale: torch.Tensor, b: torc
     n = b.shape[0]
     if b.shape[1] != k:
         raise ValueError(f"reduction dims differ: a {tuple(a.shape)}, b {tuple(b.shape)}")
+    _check_scales(layout, m, n, k, a_dscale, b_dscale, sb_n, sb_k)
     if out is None:
         if accumulate:
             raise ValueError("accumulate needs an output tensor to add to")

@@ -519,6 +519,21 @@ def test_gemm_f32_validation_on_device():
     assert torch.count_nonzero(d) == 0
 
 
+def test_wrappers_refuse_scale_tensors_too_small():
+    """The Python wrappers check the scale tensors' extents before enqueueing anything."""
+    a = torch.zeros((256, 256), dtype=torch.uint8, device=DEV)
+    sa, sw = torch.ones((2, 256), device=DEV), torch.ones((2, 2), device=DEV)
+    with pytest.raises(ValueError, match="b_dscale"):
+        pf8.fprop(a, sa, a, torch.ones((1, 2), device=DEV))       # one tile row of W's scales for two
+    with pytest.raises(ValueError, match="a_dscale"):
+        pf8.fprop(a, sa[:1], a, sw)                               # one K block of X's scales for two
+    with pytest.raises(ValueError, match="b_dscale"):
+        pf8.wgrad_f32(a, sa, a, torch.ones((2, 255), device=DEV))  # a column of X's scales short
+    y = pf8.fprop(a, sa, a, sw)                    # the right sizes still run
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y) == 0
+
+
 # ---- plain BF16 GEMM (comparison kernel) against float64 A . B^T ----
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 128), (3, 130, 256), (257, 129, 384), (640, 448, 2048), (2309, 1000, 640),

@@ -50,3 +50,28 @@ def test_fp8_linear_checks_weight_codes_before_any_launch():
     for codes in bad:
         with pytest.raises(ValueError, match="w_codes"):
             fp8_linear(x, w, None, codes)
+
+
+def test_scale_extents_are_checked_on_the_host():
+    """Scale tensors too small for the GEMM's shape and strides are refused before any launch."""
+    import pytest
+    import torch
+    from fp8_block_scaled_pf8_amd import _lib as L
+
+    m, n, k = 300, 200, 384                       # ragged M and N, 3 K blocks
+    f = lambda *s: torch.zeros(s, dtype=torch.float32)  # noqa: E731
+    sa, sw = f(3, m), f(2, 3)                     # X groups [K/128, M]; W tile grid [ceil(N/128), K/128]
+    ops._check_scales(L.PF8_FPROP, m, n, k, sa, sw, sw.stride(0), 1)
+    ops._check_scales(L.PF8_DGRAD, m, 3 * 128, 2 * 128, f(2, m), sw, 1, sw.stride(0))  # W^T: grid read transposed
+    ops._check_scales(L.PF8_WGRAD, m, n, k, sa, f(3, n), 1, n)
+    ops._check_scales(L.PF8_FPROP, m, n, k, sa, f(4, 5)[1:3, 1:4], 5, 1)  # a view: storage runs past it
+    bad = [
+        (L.PF8_FPROP, sa[:2], sw, 3, 1),           # a_dscale misses a K block
+        (L.PF8_FPROP, sa[:, :m - 1], sw, 3, 1),    # a_dscale misses a row
+        (L.PF8_FPROP, sa, f(1, 3), 3, 1),          # one tile row of W for two
+        (L.PF8_WGRAD, sa, f(3, n - 1), 1, n - 1),  # one column short
+        (L.PF8_FPROP, sa, sw, 0, 1),               # a zero stride
+    ]
+    for layout, a_s, b_s, sb_n, sb_k in bad:
+        with pytest.raises(ValueError):
+            ops._check_scales(layout, m, n, k, a_s, b_s, sb_n, sb_k)
