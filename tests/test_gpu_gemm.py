@@ -342,6 +342,48 @@ def test_linear_step_on_a_side_stream_and_in_a_graph():
             assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), f"replay {rep}"
 
 
+def test_linear_steps_from_concurrent_host_threads():
+    """The ABI keeps no state, so host threads may enqueue at once: four threads, each with its own
+    layer step on its own stream, run 10 steps each; every result equals the step's lone run."""
+    import threading
+    t = generate("tiny_fprop")
+    steps = []
+    for i in range(4):
+        dyb = _rand_bits((256, 384), 50 + i, 1e-3, outliers=False)
+        x = to_dev_bf16(t["X"]) * (1.0 + 0.25 * i)
+        steps.append(pf8.LinearStep(x, to_dev_bf16(t["W"]), to_dev_bf16(dyb)))
+    outs = lambda st: [o.clone() for o in (st.y, st.dx, st.dw, st.qxt, st.sdyt)]  # noqa: E731
+    want = []
+    for st in steps:
+        st.run()
+        torch.cuda.synchronize()
+        want.append(outs(st))
+        for o in (st.y, st.dx, st.dw):
+            o.fill_(float("nan"))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in steps]
+    errors = []
+
+    def worker(st, stream):
+        try:
+            with torch.cuda.stream(stream):
+                for _ in range(10):
+                    st.run()
+        except Exception as e:  # reported below, on the test's thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(st, sm)) for st, sm in zip(steps, streams)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=60)
+    torch.cuda.synchronize()
+    assert not errors and not any(th.is_alive() for th in threads), errors
+    for i, st in enumerate(steps):
+        for got, ref in zip(outs(st), want[i]):
+            assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), f"step {i}"
+
+
 def test_layer_step_workload_sampled():
     """The benchmark's gate+up layer pass at full size: sampled codes and outputs against the oracle.
 
