@@ -18,6 +18,9 @@
  *  - Leading dimensions ("ld") are in elements of the array they describe.
  *  - Every argument is validated on the host before anything is enqueued; on error nothing
  *    runs and the call returns the status. A launch failure is reported as PF8_ELAUNCH.
+ *    Only the sizes of buffers are out of the library's sight: each buffer must hold every
+ *    element its shape, pitch and strides address (the Python binding checks this for the
+ *    tensors it is given); a smaller one is read or written out of bounds on the device.
  *  - Scales are dequantisation multipliers: value = scale * decode(code). The quantisers write
  *    exact powers of two 2^e, e in [-126, 120]; an all-zero block gets scale 1.
  *  - E4M3 is the OCP E4M3FN encoding (bias 7, max 448, no infinities), rounded to nearest-even,
