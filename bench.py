@@ -460,6 +460,16 @@ def main():
     torch.cuda.synchronize()
     f32_us = e0.elapsed_time(e1) * 1e3 / 20
     del main_grad
+    # a later micro-batch of the same optimizer step: W's codes (made by the steps above) reused
+    for _ in range(3):
+        step.run(weight_codes=False)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(args.steps):
+        step.run(weight_codes=False)
+    e1.record(st)
+    torch.cuda.synchronize()
+    mb_ms = e0.elapsed_time(e1) / args.steps
     # cold-cache (L2 and Infinity Cache evicted before every launch) against warm timing of the
     # headline GEMM and of the dY quantiser, on the step's own buffers
     thunks = dict(step.launches())
@@ -488,6 +498,10 @@ def main():
         "kernels": kernels,
         "wgrad_f32_accumulate": {"us": round(f32_us, 2), "tflops": round(2.0 * m * n * k / (f32_us * 1e-6) / 1e12, 1),
                                  "note": "dW in FP32 added to a main gradient (not part of the step)"},
+        "micro_batch_step": {"ms_per_step": round(mb_ms, 4), "tflops": round(flops / (mb_ms * 1e-3) / 1e12, 1),
+                             "launches": len(step.launches(weight_codes=False)),
+                             "note": "the step of a later micro-batch of one optimizer step: W's codes reused, "
+                                     "X's dual quantiser alone (not the headline value)"},
         "cache": cache,
         "peak_device": device_peak_fp8(),
     }

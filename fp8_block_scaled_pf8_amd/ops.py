@@ -255,7 +255,9 @@ class LinearStep:
     With ``fused`` (the default; needs M, N, K multiples of 128) X and dY are each read once by
     the dual-orientation quantiser, and X's and W's quantisers share one launch: five launches.
     Otherwise each orientation has its own pass: eight launches. ``run`` enqueues them on the
-    current stream and allocates nothing.
+    current stream and allocates nothing. ``run(weight_codes=False)`` is the step of a later
+    micro-batch of the same optimizer step: W's codes from an earlier full run are reused, and
+    X's dual quantiser runs alone.
     """
 
     def __init__(self, x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, variant: int = L.PF8_GEMM_AUTO,
@@ -284,8 +286,9 @@ class LinearStep:
     def flops(self) -> int:
         return 3 * 2 * self.m * self.n * self.k
 
-    def launches(self):
-        """The step as a list of (name, thunk); each thunk enqueues one kernel and returns its status."""
+    def launches(self, weight_codes: bool = True):
+        """The step as a list of (name, thunk); each thunk enqueues one kernel and returns its status.
+        Without ``weight_codes`` W is not quantised (its codes must come from an earlier run)."""
         st = torch.cuda.current_stream(self.x.device).cuda_stream
         m, n, k, v = self.m, self.n, self.k, self.variant
         x, dy = self.x, self.dy
@@ -324,9 +327,10 @@ class LinearStep:
             v, L.PF8_WGRAD, n, k, m, self.qdyt.data_ptr(), lqdyt, self.sdyt.data_ptr(), n, self.qxt.data_ptr(), lqxt,
             self.sxt.data_ptr(), 1, k, self.dw.data_ptr(), ldw, st))
         if self.fused:
-            return [quant_fwd, fprop, quant_dy_dual, dgrad, wgrad]
-        return [quant_x_rows, quant_w, fprop, quant_dy_rows, dgrad, quant_dy_cols, quant_x_cols, wgrad]
+            return [quant_fwd if weight_codes else quant_x_dual, fprop, quant_dy_dual, dgrad, wgrad]
+        return ([quant_x_rows] + ([quant_w] if weight_codes else []) +
+                [fprop, quant_dy_rows, dgrad, quant_dy_cols, quant_x_cols, wgrad])
 
-    def run(self) -> None:
-        for name, launch in self.launches():
+    def run(self, weight_codes: bool = True) -> None:
+        for name, launch in self.launches(weight_codes):
             L.check(launch(), name)

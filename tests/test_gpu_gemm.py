@@ -303,6 +303,28 @@ def test_linear_step_matches_oracle(fused):
     _report(bf16_f64(step.dw), oracle.gemm_wgrad(qdyt, sdyt, qxt, sxt), "step wgrad")
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["dual_quant", "single_quant"])
+def test_linear_step_reusing_weight_codes(fused):
+    """A later micro-batch's step (W's codes from an earlier run, one launch fewer) gives the full
+    step's results bit for bit."""
+    t = generate("tiny_fprop")
+    dyb = _rand_bits((256, 384), 47, 1e-3, outliers=False)
+    step = pf8.LinearStep(to_dev_bf16(t["X"]), to_dev_bf16(t["W"]), to_dev_bf16(dyb), fused=fused)
+    assert len(step.launches(weight_codes=False)) == len(step.launches()) - (0 if fused else 1)
+    step.run()
+    torch.cuda.synchronize()
+    outs = lambda: [o.clone() for o in (step.y, step.dx, step.dw, step.qx, step.qxt, step.sx, step.sxt)]  # noqa: E731
+    want = outs()
+    for o in (step.y, step.dx, step.dw):
+        o.fill_(float("nan"))
+    for o in (step.qx, step.qxt, step.sx, step.sxt):
+        o.fill_(0)
+    step.run(weight_codes=False)
+    torch.cuda.synchronize()
+    for got, ref in zip(outs(), want):
+        assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8))
+
+
 def test_linear_step_on_a_side_stream_and_in_a_graph():
     """The library enqueues on the caller's stream and allocates nothing, so the step runs on a
     side stream and replays from a captured HIP graph. Every replay (with eager work in between
