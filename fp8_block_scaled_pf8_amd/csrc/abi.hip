@@ -32,7 +32,7 @@ extern "C" {
 
 int pf8_abi_version(void) { return PF8_ABI_VERSION; }
 
-const char* pf8_strerror(int status) {
+const char* pf8_strerror(pf8_status status) {
   switch (status) {
     case PF8_OK: return "ok";
     case PF8_EINVAL: return "invalid argument (null pointer, unknown enum, non-positive dimension or leading dimension too small)";
@@ -44,7 +44,7 @@ const char* pf8_strerror(int status) {
   }
 }
 
-int pf8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx, int axis, void* q, int64_t ldq,
+pf8_status pf8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx, pf8_group_axis axis, void* q, int64_t ldq,
                         float* dscale, int64_t ld_s, void* hip_stream) {
   if (x == nullptr || q == nullptr || dscale == nullptr) return PF8_EINVAL;
   if (axis != PF8_ALONG_COLS && axis != PF8_ALONG_ROWS) return PF8_EINVAL;
@@ -67,7 +67,7 @@ int pf8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx, 
   return launch_status(e);
 }
 
-int pf8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q_row, int64_t ldq_row,
+pf8_status pf8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q_row, int64_t ldq_row,
                        float* dscale_row, int64_t ld_sr, void* q_col, int64_t ldq_col, float* dscale_col, int64_t ld_sc,
                        void* hip_stream) {
   if (x == nullptr || q_row == nullptr || dscale_row == nullptr || q_col == nullptr || dscale_col == nullptr)
@@ -84,7 +84,7 @@ int pf8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, v
                                               dscale_col, ld_sc, static_cast<hipStream_t>(hip_stream)));
 }
 
-int pf8_quant_fwd(const void* x, int64_t m, int64_t k, int64_t ldx, void* qx, int64_t ldqx, float* sx, int64_t ld_sx,
+pf8_status pf8_quant_fwd(const void* x, int64_t m, int64_t k, int64_t ldx, void* qx, int64_t ldqx, float* sx, int64_t ld_sx,
                   void* qxt, int64_t ldqxt, float* sxt, int64_t ld_sxt, const void* w, int64_t n, int64_t ldw, void* qw,
                   int64_t ldqw, void* qwt, int64_t ldqwt, float* sw, int64_t ld_sw, void* hip_stream) {
   if (x == nullptr || qx == nullptr || sx == nullptr || qxt == nullptr || sxt == nullptr || w == nullptr ||
@@ -105,7 +105,7 @@ int pf8_quant_fwd(const void* x, int64_t m, int64_t k, int64_t ldx, void* qx, in
                                              ldqw, qwt, ldqwt, sw, ld_sw, static_cast<hipStream_t>(hip_stream)));
 }
 
-int pf8_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw, void* q, int64_t ldq, void* qt, int64_t ldqt,
+pf8_status pf8_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw, void* q, int64_t ldq, void* qt, int64_t ldqt,
                         float* dscale, int64_t ld_s, void* hip_stream) {
   if (w == nullptr || q == nullptr || dscale == nullptr) return PF8_EINVAL;
   if (n <= 0 || k <= 0) return PF8_EINVAL;
@@ -119,7 +119,7 @@ int pf8_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw, void* 
                                            static_cast<hipStream_t>(hip_stream)));
 }
 
-int pf8_block_gemm_variant(int variant, int layout, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda,
+pf8_status pf8_block_gemm_variant(int variant, pf8_layout layout, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda,
                            const float* a_dscale, int64_t ld_as, const void* b, int64_t ldb, const float* b_dscale,
                            int64_t sb_n, int64_t sb_k, void* d, int64_t ldd, void* hip_stream) {
   if (variant != PF8_GEMM_AUTO && variant != PF8_GEMM_MX_SCALED && variant != PF8_GEMM_PROMOTE) return PF8_EINVAL;
@@ -139,7 +139,7 @@ int pf8_block_gemm_variant(int variant, int layout, int64_t m, int64_t n, int64_
   return launch_status(pf8::launch_gemm(args, layout == PF8_WGRAD, mx, static_cast<hipStream_t>(hip_stream)));
 }
 
-int pf8_block_gemm_f32(int layout, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const float* a_dscale,
+pf8_status pf8_block_gemm_f32(pf8_layout layout, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const float* a_dscale,
                        int64_t ld_as, const void* b, int64_t ldb, const float* b_dscale, int64_t sb_n, int64_t sb_k,
                        float* d, int64_t ldd, int accumulate, void* hip_stream) {
   if (layout != PF8_FPROP && layout != PF8_DGRAD && layout != PF8_WGRAD) return PF8_EINVAL;
@@ -158,7 +158,7 @@ int pf8_block_gemm_f32(int layout, int64_t m, int64_t n, int64_t k, const void* 
   return launch_status(pf8::launch_gemm(args, layout == PF8_WGRAD, true, static_cast<hipStream_t>(hip_stream)));
 }
 
-int pf8_gemm_bf16(int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const void* b, int64_t ldb, void* d,
+pf8_status pf8_gemm_bf16(int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const void* b, int64_t ldb, void* d,
                   int64_t ldd, void* hip_stream) {
   if (a == nullptr || b == nullptr || d == nullptr) return PF8_EINVAL;
   if (m <= 0 || n <= 0 || k <= 0) return PF8_EINVAL;
@@ -175,7 +175,7 @@ int pf8_gemm_bf16(int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, c
   return launch_status(pf8::launch_gemm_bf16(args, static_cast<hipStream_t>(hip_stream)));
 }
 
-int pf8_block_gemm(int layout, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const float* a_dscale,
+pf8_status pf8_block_gemm(pf8_layout layout, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const float* a_dscale,
                    int64_t ld_as, const void* b, int64_t ldb, const float* b_dscale, int64_t sb_n, int64_t sb_k,
                    void* d, int64_t ldd, void* hip_stream) {
   return pf8_block_gemm_variant(PF8_GEMM_AUTO, layout, m, n, k, a, lda, a_dscale, ld_as, b, ldb, b_dscale, sb_n, sb_k,

@@ -131,21 +131,38 @@ class Fp8Linear(torch.nn.Module):
             self.weight.main_grad = torch.zeros(self.weight.shape, dtype=torch.float32, device=self.weight.device)
         self._codes = None
         self._codes_key = None
+        self._codes_ready = None  # event recorded on the stream that made the codes
+        self._codes_users = set()  # streams the codes were handed to
 
     def weight_codes(self) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-        """W's codes, transposed codes and tile scales, made once per version of the weight."""
+        """W's codes, transposed codes and tile scales, made once per version of the weight.
+
+        They are made on the current stream. A later call from another stream makes that stream
+        wait for them, and marks them as used there, so that the allocator keeps their memory
+        until that stream's work is done even after new codes replace them."""
         w = self.weight
         key = (w.data_ptr(), w._version, tuple(w.shape), w.device)
+        cur = torch.cuda.current_stream(w.device)
         if self._codes is None or self._codes_key != key:
             with torch.no_grad():
                 self._codes = ops.quant_w_128x128(w.detach().contiguous(), transposed=True)
             self._codes_key = key
+            self._codes_ready = torch.cuda.Event()
+            self._codes_ready.record(cur)
+            self._codes_users = {cur.cuda_stream}
+        elif cur.cuda_stream not in self._codes_users:
+            cur.wait_event(self._codes_ready)
+            for t in self._codes:
+                t.record_stream(cur)
+            self._codes_users.add(cur.cuda_stream)
         return self._codes
 
     def invalidate_weight_codes(self) -> None:
         """Forget the cached weight codes (after a change to W that its version counter misses)."""
         self._codes = None
         self._codes_key = None
+        self._codes_ready = None
+        self._codes_users = set()
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         return fp8_linear(x, self.weight, getattr(self.weight, "main_grad", None), self.weight_codes())

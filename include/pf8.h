@@ -44,7 +44,14 @@ extern "C" {
 
 #define PF8_ABI_VERSION 5
 
-/* Status codes (int). */
+/* The status, grouping-axis and layout types are plain ints, so that an out-of-range value
+   reaches the library intact and is refused with PF8_EINVAL (a C enum parameter need not be
+   able to carry such a value). The names below are their only valid values. */
+typedef int pf8_status;
+typedef int pf8_group_axis;
+typedef int pf8_layout;
+
+/* Status codes (pf8_status). */
 #define PF8_OK 0
 #define PF8_EINVAL 1  /* null pointer, unknown enum value, non-positive dimension, ld too small */
 #define PF8_ESHAPE 2  /* a grouped / tiled dimension is not a multiple of 128 (or 8, see below) */
@@ -52,11 +59,11 @@ extern "C" {
 #define PF8_ENODEV 4  /* no usable HIP device (the library loads and validates without one) */
 #define PF8_ELAUNCH 5 /* the kernel launch reported an error */
 
-/* Grouping axis of the activation / gradient quantiser. */
+/* Grouping axis of the activation / gradient quantiser (pf8_group_axis). */
 #define PF8_ALONG_COLS 0 /* row mode: a group is 128 consecutive elements of one row */
 #define PF8_ALONG_ROWS 1 /* col mode: a group is 128 consecutive rows of one column; codes are written transposed */
 
-/* GEMM layouts. */
+/* GEMM layouts (pf8_layout). */
 #define PF8_FPROP 0 /* Y[M,N]  = X[M,K] . W[N,K]^T       B = W codes, one scale per 128x128 tile      */
 #define PF8_DGRAD 1 /* dX[M,K] = dY[M,N] . W[N,K]        B = W^T codes [K,N], W's tile scales via strides */
 #define PF8_WGRAD 2 /* dW[N,K] = dY[M,N]^T . X[M,K]      B = X^T codes [K,M], one scale per (128-block, row) */
@@ -82,8 +89,8 @@ extern "C" {
  *     dscale: f32 [rows/128][cols], i.e. dscale[g * ld_s + c]; ld_s >= cols.
  * Returns PF8_OK, PF8_EINVAL, PF8_ESHAPE, PF8_EALIGN, PF8_ENODEV or PF8_ELAUNCH.
  */
-int pf8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx, int axis,
-                        void* q, int64_t ldq, float* dscale, int64_t ld_s, void* hip_stream);
+pf8_status pf8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx, pf8_group_axis axis,
+                               void* q, int64_t ldq, float* dscale, int64_t ld_s, void* hip_stream);
 
 /*
  * Dual-orientation 1x128 quantiser [same passages as above; the forward pass needs X grouped
@@ -98,9 +105,9 @@ int pf8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx, 
  * The four outputs are bit-identical to those of the two single-orientation calls.
  * Returns PF8_OK, PF8_EINVAL, PF8_ESHAPE, PF8_EALIGN, PF8_ENODEV or PF8_ELAUNCH.
  */
-int pf8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx,
-                       void* q_row, int64_t ldq_row, float* dscale_row, int64_t ld_sr,
-                       void* q_col, int64_t ldq_col, float* dscale_col, int64_t ld_sc, void* hip_stream);
+pf8_status pf8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                              void* q_row, int64_t ldq_row, float* dscale_row, int64_t ld_sr,
+                              void* q_col, int64_t ldq_col, float* dscale_col, int64_t ld_sc, void* hip_stream);
 
 /*
  * Forward-pass quantisers of one linear layer in one launch [the passages above: X grouped along
@@ -113,11 +120,11 @@ int pf8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx,
  * W: bf16 [n, k], pitch ldw; qw, qwt (may be NULL), sw as q, qt, dscale of pf8_quant_w_128x128.
  * m, n and k must be multiples of 128. The outputs are bit-identical to the two separate calls.
  */
-int pf8_quant_fwd(const void* x, int64_t m, int64_t k, int64_t ldx,
-                  void* qx, int64_t ldqx, float* sx, int64_t ld_sx,
-                  void* qxt, int64_t ldqxt, float* sxt, int64_t ld_sxt,
-                  const void* w, int64_t n, int64_t ldw,
-                  void* qw, int64_t ldqw, void* qwt, int64_t ldqwt, float* sw, int64_t ld_sw, void* hip_stream);
+pf8_status pf8_quant_fwd(const void* x, int64_t m, int64_t k, int64_t ldx,
+                         void* qx, int64_t ldqx, float* sx, int64_t ld_sx,
+                         void* qxt, int64_t ldqxt, float* sxt, int64_t ld_sxt,
+                         const void* w, int64_t n, int64_t ldw,
+                         void* qw, int64_t ldqw, void* qwt, int64_t ldqwt, float* sw, int64_t ld_sw, void* hip_stream);
 
 /*
  * 128x128 weight-tile quantiser [paper.rainbus.top summary, section "FP8 块级混合精度训练" and
@@ -128,8 +135,8 @@ int pf8_quant_fwd(const void* x, int64_t m, int64_t k, int64_t ldx,
  * qt:     u8 [k, n] (the same codes transposed, for the data-gradient GEMM) or NULL; pitch ldqt >= n.
  * dscale: f32 [n/128][k/128], i.e. dscale[tn * ld_s + tk]; ld_s >= k/128.
  */
-int pf8_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw, void* q, int64_t ldq,
-                        void* qt, int64_t ldqt, float* dscale, int64_t ld_s, void* hip_stream);
+pf8_status pf8_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw, void* q, int64_t ldq,
+                               void* qt, int64_t ldqt, float* dscale, int64_t ld_s, void* hip_stream);
 
 /*
  * Block-scaled FP8 GEMM [paperlayer.ai summary, appendix C, bullet "FP8 implementation pipeline":
@@ -138,6 +145,20 @@ int pf8_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw, void* 
  *   D[i, j] = sum_{kb} sa(kb, i) * sb(kb, j) * sum_{k in block kb} decode(A[i, k]) * decode(B[j, k])
  *
  * with FP32 accumulation and a BF16 (round-to-nearest-even) result.
+ *
+ * Accumulation contract. On gfx950's FP8 matrix instructions (both variants; measured) the
+ * products of each aligned group of 8 consecutive k are exact and are added in a fixed-point
+ * window: each is truncated toward zero to a multiple of 2^(E-13), where 2^E <= the group's
+ * largest |product| < 2^(E+1). Group sums accumulate in FP32. With ref = the exact sum above and
+ * p_k = sa * decode(A[i,k]) * sb * decode(B[j,k]), every element therefore satisfies
+ *     |D[i,j] - ref| <= 2^-8 |ref| + (1 + 2^-8) * (7 * 2^-13 * sum_{groups g} max_{k in g} |p_k|
+ *                                                  + (k / 4) * 2^-24 * sum_k |p_k|)
+ * (window truncation, fewer than k/4 FP32 roundings, BF16 rounding). On operands distributed like
+ * training activations with rare outliers against Gaussian weights or gradients, the error also
+ * stays within |D[i,j] - ref| <= 2^-7 |ref| + 1e-3 rms(ref) (rms over the whole output), the bar
+ * the library is tested to on such data. With outliers in both operands an outlier product can
+ * take the low bits of the other seven products of its group, and only the contract holds.
+ *
  * m, n >= 1 (any value), k % 128 == 0.
  * a: u8 [m, k] (pitch lda >= k), reduction dim contiguous.  a_dscale: f32, sa(kb, i) = a_dscale[kb * ld_as + i], ld_as >= m.
  * b: u8 [n, k] (pitch ldb >= k), reduction dim contiguous.  b_dscale: f32, with
@@ -150,16 +171,16 @@ int pf8_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw, void* 
  * The MX-scaled variant needs every scale to be an exact power of two in [2^-127, 2^127] (what the
  * quantisers produce); PF8_GEMM_PROMOTE accepts any finite FP32 scales.
  */
-int pf8_block_gemm(int layout, int64_t m, int64_t n, int64_t k,
-                   const void* a, int64_t lda, const float* a_dscale, int64_t ld_as,
-                   const void* b, int64_t ldb, const float* b_dscale, int64_t sb_n, int64_t sb_k,
-                   void* d, int64_t ldd, void* hip_stream);
+pf8_status pf8_block_gemm(pf8_layout layout, int64_t m, int64_t n, int64_t k,
+                          const void* a, int64_t lda, const float* a_dscale, int64_t ld_as,
+                          const void* b, int64_t ldb, const float* b_dscale, int64_t sb_n, int64_t sb_k,
+                          void* d, int64_t ldd, void* hip_stream);
 
 /* Same as pf8_block_gemm with an explicit kernel variant (PF8_GEMM_*); PF8_EINVAL for an unknown one. */
-int pf8_block_gemm_variant(int variant, int layout, int64_t m, int64_t n, int64_t k,
-                           const void* a, int64_t lda, const float* a_dscale, int64_t ld_as,
-                           const void* b, int64_t ldb, const float* b_dscale, int64_t sb_n, int64_t sb_k,
-                           void* d, int64_t ldd, void* hip_stream);
+pf8_status pf8_block_gemm_variant(int variant, pf8_layout layout, int64_t m, int64_t n, int64_t k,
+                                  const void* a, int64_t lda, const float* a_dscale, int64_t ld_as,
+                                  const void* b, int64_t ldb, const float* b_dscale, int64_t sb_n, int64_t sb_k,
+                                  void* d, int64_t ldd, void* hip_stream);
 
 /*
  * Block-scaled FP8 GEMM with an FP32 result [paperlayer.ai summary, appendix C "Production
@@ -170,15 +191,17 @@ int pf8_block_gemm_variant(int variant, int layout, int64_t m, int64_t n, int64_
  *   accumulate = 1:  D[i, j] += (the same sum)
  *
  * Layouts, operands, scales and limits are exactly those of pf8_block_gemm; the product is formed
- * by the MX-scaled kernel with FP32 accumulation and is not rounded to BF16.
+ * by the MX-scaled kernel with FP32 accumulation and is not rounded to BF16. The accumulation
+ * contract of pf8_block_gemm holds for the product without its 2^-8 |ref| (BF16) term; with
+ * accumulate = 1 the final FP32 addition rounds once more.
  * d: f32 [m, n], row pitch ldd >= n with ldd * 4 a multiple of 16 bytes, 16-byte aligned base.
  * With accumulate = 1 every element of d is read once and written once by a single thread (no
  * atomics); d must not overlap a or b. accumulate other than 0 or 1 is PF8_EINVAL.
  */
-int pf8_block_gemm_f32(int layout, int64_t m, int64_t n, int64_t k,
-                       const void* a, int64_t lda, const float* a_dscale, int64_t ld_as,
-                       const void* b, int64_t ldb, const float* b_dscale, int64_t sb_n, int64_t sb_k,
-                       float* d, int64_t ldd, int accumulate, void* hip_stream);
+pf8_status pf8_block_gemm_f32(pf8_layout layout, int64_t m, int64_t n, int64_t k,
+                              const void* a, int64_t lda, const float* a_dscale, int64_t ld_as,
+                              const void* b, int64_t ldb, const float* b_dscale, int64_t sb_n, int64_t sb_k,
+                              float* d, int64_t ldd, int accumulate, void* hip_stream);
 
 /*
  * Plain BF16 GEMM, the comparison point for the FP8 path [the pages measure FP8 training against
@@ -191,11 +214,11 @@ int pf8_block_gemm_f32(int layout, int64_t m, int64_t n, int64_t k,
  * operand here); d: bf16 [m, n], pitch ldd >= n. m, n >= 1 (any value), k % 128 == 0.
  * Bases 16-byte aligned, pitches multiples of 16 bytes; lda, ldb <= (2^31 - 1) / 512.
  */
-int pf8_gemm_bf16(int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const void* b, int64_t ldb,
-                  void* d, int64_t ldd, void* hip_stream);
+pf8_status pf8_gemm_bf16(int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const void* b, int64_t ldb,
+                         void* d, int64_t ldd, void* hip_stream);
 
 /* Static, NUL-terminated description of a status code ("unknown status" for other values). */
-const char* pf8_strerror(int status);
+const char* pf8_strerror(pf8_status status);
 
 /* PF8_ABI_VERSION of the loaded library. */
 int pf8_abi_version(void);

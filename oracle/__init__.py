@@ -51,6 +51,8 @@ from .gemm import (
     gemm_blockwise_exact,
     unquantized_reference,
     gemm_tolerance_report,
+    contract_allowance,
+    contract_report,
 )
 
 __all__ = [
@@ -70,4 +72,6 @@ __all__ = [
     "gemm_blockwise_exact",
     "unquantized_reference",
     "gemm_tolerance_report",
+    "contract_allowance",
+    "contract_report",
 ]

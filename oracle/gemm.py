@@ -19,6 +19,22 @@ The fast path accumulates in FP32 and writes BF16 (the pages do not fix the
 accumulator; FP32 accumulation and BF16 output are the readings taken). It is
 judged per element against the unrounded float64 value:
     |gpu - ref| <= 2^-7 * |ref| + 1e-3 * rms(ref).
+
+A second, always-applicable bound (contract_allowance) states what FP32
+accumulation delivers on a matrix unit that adds the products of each aligned
+group of 8 consecutive k in a fixed-point window: every product is truncated
+toward zero to a multiple of 2^(E-13), E = floor(log2) of the group's largest
+product magnitude, and the group sums are accumulated in FP32. Each group then
+loses less than 7 * 2^(E-13) <= 7 * 2^-13 * max_g |a b|, each FP32 rounding
+of a running sum at most 2^-24 of its magnitude (there are fewer than K/4 of
+them: K/8 group sums, plus one scale FMA per 128-block where the scales are
+applied outside the matrix instruction), and the BF16 output rounding at most
+2^-8 of the value:
+    |gpu - ref| <= 2^-8 |ref|
+                   + (1 + 2^-8) * (7 * 2^-13 * sum_g max_{k in g} |a_k b_k|
+                                   + (K/4) * 2^-24 * sum_k |a_k b_k|).
+It is a statement about the accumulator, not about the method: the method is
+the exact sum above.
 """
 from __future__ import annotations
 
@@ -30,6 +46,7 @@ import numpy as np
 from .e4m3 import decode_e4m3
 
 GROUP = 128
+WINDOW_GROUP = 8  # products summed together in one fixed-point window
 
 
 def dequant_act_groups(q: np.ndarray, dscale: np.ndarray) -> np.ndarray:
@@ -141,3 +158,33 @@ def gemm_tolerance_report(gpu: np.ndarray, ref64: np.ndarray) -> Dict[str, float
         "frac_bit_equal_bf16": float(np.mean(gpu_bits == ref_bf16)) if gpu.size else 1.0,
         "n": int(gpu.size),
     }
+
+
+def contract_allowance(a_deq: np.ndarray, b_deq: np.ndarray, ref64: np.ndarray) -> np.ndarray:
+    """Per-element allowance of the accumulation contract (module docstring) for
+    D[i, j] = sum_k a_deq[i, k] * b_deq[j, k], given the exact ref64 = that sum.
+
+    a_deq [m, K], b_deq [n, K] are the dequantised operands (float64); K % 8 == 0."""
+    a = np.abs(np.asarray(a_deq, dtype=np.float64))
+    b = np.abs(np.asarray(b_deq, dtype=np.float64))
+    m, k = a.shape
+    if b.shape[1] != k or k % WINDOW_GROUP:
+        raise ValueError("operands must share a K that is a multiple of 8")
+    abs_sum = a @ b.T
+    group_max_sum = np.zeros((m, b.shape[0]))
+    for g in range(0, k, WINDOW_GROUP):
+        gmax = np.zeros((m, b.shape[0]))
+        for kk in range(g, g + WINDOW_GROUP):
+            np.maximum(gmax, np.multiply.outer(a[:, kk], b[:, kk]), out=gmax)
+        group_max_sum += gmax
+    window = 7.0 * 2.0 ** -13 * group_max_sum + (k // 4) * 2.0 ** -24 * abs_sum
+    return 2.0 ** -8 * np.abs(np.asarray(ref64, dtype=np.float64)) + (1.0 + 2.0 ** -8) * window
+
+
+def contract_report(gpu: np.ndarray, ref64: np.ndarray, allowance: np.ndarray) -> Dict[str, float]:
+    """Elements outside the accumulation contract's allowance, and the worst error / allowance."""
+    err = np.abs(np.asarray(gpu, dtype=np.float64) - np.asarray(ref64, dtype=np.float64))
+    allowance = np.asarray(allowance, dtype=np.float64)
+    viol = int(np.count_nonzero(~(err <= allowance)))
+    ratio = float(np.max(err / np.where(allowance > 0, allowance, 1.0))) if err.size else 0.0
+    return {"violations": viol, "max_err_over_allowance": ratio, "n": int(err.size)}

@@ -20,7 +20,7 @@ S4 = 0x40000
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(pf8_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|pf8_status|const char\*)\s+(pf8_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_every_declared_symbol_is_exported():

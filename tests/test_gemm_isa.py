@@ -88,3 +88,46 @@ def test_scale_and_operand_load_counts(asm):
             assert n == want, f"{name}: a K-loop trip issues {n} loads, expected {want}"
         checked += 1
     assert checked >= 40, checked
+
+
+def test_whole_kernel_load_totals_match_the_stage_layout(asm):
+    """Every load the stage layout issues, counted over the whole kernel: the five prologue and
+    head paths (head length h = 1, 3, 5, 7, 9), the K loop and the tail. This covers the head
+    stages, whose refills carry scale loads under the same explicit waits.
+
+    Per path with five buffers: stages 0..3 whole plus stage 4's A part (4 D + A_DMA direct-to-LDS
+    loads, scales of stages 0 and 2), then h head stages, each finishing one refill and starting
+    the next (D loads, scales when the finished refill's stage is even, i.e. for (h + 1) / 2 of
+    them). The loop trip holds 10 D loads and 5 scale sets; the tail finishes the last refill
+    (B_DMA loads of an odd stage, no scales). With two buffers: stage 0 and stage 1's A part, a
+    two-stage loop trip, and the tail's B part."""
+    kern = re.compile(r"_ZN3pf814gemm_mx_kernelILi(\d+)ELi(\d+)ELb(\d)ELb(\d)ELi(\d)ELb(\d)ELb(\d)E")
+    checked = 0
+    for name, body in _functions(asm).items():
+        m = kern.match(name)
+        if not m:
+            continue
+        bm, bn, row_b, _, nst, f32, bf16in = (int(x) for x in m.groups())
+        wm, wn = bm // 2, bn // 2
+        tm, tn = wm // 32, wn // 32
+        sb = 1 if (not row_b and 128 % wn == 0) else tn
+        a_dma, b_dma = bm // 64, bn // 64
+        d = a_dma + b_dma
+        ss = 0 if bf16in else tm + sb
+        heads = (1, 3, 5, 7, 9)
+        if nst == 5:
+            want_lds = sum(4 * d + a_dma + h * d for h in heads) + 10 * d + b_dma
+            want_scale = sum(2 * ss + (h + 1) // 2 * ss for h in heads) + 5 * ss
+        else:
+            want_lds = d + a_dma + 2 * d + b_dma
+            want_scale = ss + ss
+        lds = sum(1 for ln in body if ln.strip().startswith("buffer_load_dword") and " lds" in ln)
+        scale = sum(1 for ln in body if ln.strip().startswith("global_load_dword "))
+        assert lds == want_lds, f"{name}: {lds} direct-to-LDS loads, expected {want_lds}"
+        if f32:
+            # the FP32 epilogue's edge path reads old values one float at a time with the same opcode
+            assert scale >= want_scale, f"{name}: {scale} dword loads, expected at least {want_scale}"
+        else:
+            assert scale == want_scale, f"{name}: {scale} scale loads, expected {want_scale}"
+        checked += 1
+    assert checked >= 40, checked

@@ -149,3 +149,30 @@ def test_fp8_linear_weight_codes_follow_the_weight():
     layer.invalidate_weight_codes()
     forward_checked("Y after a .data write and invalidate_weight_codes()")
     assert layer.weight_codes() is not codes
+
+
+def test_fp8_linear_weight_codes_on_another_stream():
+    """Codes made on one stream and used by a forward on another: the second stream waits for them
+    (the main stream makes them behind a long sleep, so a side stream that did not wait would read
+    unfinished codes), and the result equals the one on the main stream."""
+    m, k, n = 256, 384, 256
+    layer = pf8.Fp8Linear(k, n, device=DEV, weight=to_dev_bf16(_bits((n, k), 61, 0.02, False)))
+    x = to_dev_bf16(_bits((m, k), 62, 1.0, True))
+    with torch.no_grad():
+        y_main = layer(x)
+    torch.cuda.synchronize()
+    layer.weight.data.mul_(0.5)
+    layer.invalidate_weight_codes()
+    side = torch.cuda.Stream()
+    torch.cuda._sleep(20_000_000)        # keep the main stream busy before it makes the new codes
+    codes = layer.weight_codes()          # enqueued behind the sleep, on the main stream
+    with torch.cuda.stream(side):
+        with torch.no_grad():
+            y_side = layer(x)
+        assert layer.weight_codes() is codes
+    torch.cuda.synchronize()
+    with torch.no_grad():
+        y_again = layer(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y_side, y_again)
+    assert not torch.equal(y_side, y_main)

@@ -2,7 +2,8 @@
 
 Exact rational sums on tiny shapes, closed forms (identity, one-hot,
 permutation and power-of-two-scaled weights), a hand-derived worked example,
-and the sanity bound on quantisation error against the unquantised product.
+the sanity bound on quantisation error against the unquantised product, and the
+two parity checkers: the per-element bar and the accumulation contract.
 """
 import json
 import os
@@ -13,6 +14,8 @@ import pytest
 
 from oracle import (
     bf16_round_from_f64,
+    contract_allowance,
+    contract_report,
     decode_e4m3,
     gemm_blockwise_exact,
     gemm_dgrad,
@@ -169,32 +172,99 @@ def test_tolerance_report_flags_violations():
     assert gemm_tolerance_report(bad, ref)["violations"] == 1
 
 
+# The bar, per element: |gpu - ref| <= 2^-7 |ref| + 1e-3 rms(ref), rms over every compared
+# reference value. The bounds below are worked out by hand, with values chosen so that every
+# quantity is exact in float64.
+
+def test_tolerance_bound_is_inclusive_and_exact_at_its_edge():
+    # ref = 1000 everywhere: rms = 1000, 1e-3 * rms = 1 exactly, 2^-7 * 1000 = 7.8125,
+    # so the bound is 8.8125 for every element
+    ref = np.full(4096, 1000.0)
+    gpu = ref.copy()
+    gpu[5] = 1000.0 + 8.8125   # on the bound, above
+    gpu[6] = 1000.0 - 8.8125   # on the bound, below
+    rep = gemm_tolerance_report(gpu, ref)
+    assert rep["violations"] == 0
+    assert rep["rms_ref"] == 1000.0 and rep["max_err_over_bound"] == 1.0
+    gpu[7] = np.nextafter(1000.0 + 8.8125, np.inf)  # one float64 ulp past it
+    gpu[8] = np.nextafter(1000.0 - 8.8125, -np.inf)
+    assert gemm_tolerance_report(gpu, ref)["violations"] == 2
+
+
+def test_tolerance_bound_separates_adjacent_bf16_values():
+    # ref = 896 everywhere (a bf16 value; bf16 spacing is 4 in [512, 1024)):
+    # bound = 2^-7 * 896 + 1e-3 * 896 = 7 + 0.896 = 7.896, so the bf16 neighbours 900 and 892
+    # (error 4) pass while 904 and 888 (error 8), one bf16 ulp further, fail
+    ref = np.full(64, 896.0)
+    for ok_val, bad_val in ((900.0, 904.0), (892.0, 888.0)):
+        gpu = ref.copy()
+        gpu[3] = ok_val
+        assert gemm_tolerance_report(gpu, ref)["violations"] == 0
+        gpu[3] = bad_val
+        assert gemm_tolerance_report(gpu, ref)["violations"] == 1
+
+
+def test_tolerance_relative_term_is_two_to_minus_seven():
+    # one large reference value among zeros: ref = [256, 0 x 65535], rms = 256 / 256 = 1,
+    # bound at element 0 = 2 + 0.001; an error of 3 is outside 2^-7 * 256 + 1e-3 but would be
+    # inside 2^-6 * 256 + 1e-3 = 4.001, and an error of 2 is inside
+    ref = np.zeros(65536)
+    ref[0] = 256.0
+    gpu = ref.copy()
+    gpu[0] = 258.0
+    assert gemm_tolerance_report(gpu, ref)["violations"] == 0
+    gpu[0] = 259.0
+    rep = gemm_tolerance_report(gpu, ref)
+    assert rep["violations"] == 1 and rep["rms_ref"] == 1.0
+    assert abs(rep["max_err_over_bound"] - 3.0 / 2.001) < 1e-12
+
+
+def test_tolerance_absolute_term_uses_the_reference_rms():
+    # ref = [1, 0 x 999]: rms(ref) = sqrt(1/1000) = 0.0316..., so the bound at a zero reference
+    # is 3.16e-5. gpu carries a gross error of 100 at element 1 (a violation whichever rms is
+    # used) and an error of 1e-3 at element 2: outside 1e-3 * rms(ref) = 3.2e-5, but inside
+    # 1e-3 * rms(gpu) = 1e-3 * sqrt((1 + 100^2 + 1e-6) / 1000) = 3.2e-3. Taking the rms over the
+    # GPU values would hide the second violation.
+    ref = np.zeros(1000)
+    ref[0] = 1.0
+    gpu = ref.copy()
+    gpu[1] = 100.0
+    gpu[2] = 1e-3
+    rep = gemm_tolerance_report(gpu, ref)
+    assert rep["violations"] == 2
+    assert abs(rep["rms_ref"] - np.sqrt(1e-3)) < 1e-15
+    # an all-zero reference has rms 0: only exact zeros pass
+    z = np.zeros(8)
+    assert gemm_tolerance_report(z, z)["violations"] == 0
+    assert gemm_tolerance_report(np.full(8, 2.0 ** -149), z)["violations"] == 8
+
+
 @pytest.mark.parametrize("key", ["tiny_fprop", "attn_fprop", "mlp_gateup_fprop", "mlp_down_fprop_dgrad", "wgrad"])
 def test_quantisation_error_sanity_bound(key):
-    """||ref64 - A.B^T||_F / ||A.B^T||_F <= 0.05 on the configured distributions (rows truncated to 1024)."""
+    """||ref64 - A.B^T||_F / ||A.B^T||_F <= 0.05 on every configuration at its full size (the
+    oracle's block-scaled product against the float64 product of the unquantised bf16 inputs)."""
     t = generate(key)
-    rows = 1024
+
+    def rel(got, ref):
+        return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
     if key == "wgrad":
-        dy, x = t["dY"][:rows], t["X"][:rows, :1024]
+        dy, x = t["dY"], t["X"]
         qdyt, sdy = quant_act_1x128(dy, "rows")
         qxt, sx = quant_act_1x128(x, "rows")
-        got = gemm_wgrad(qdyt, sdy, qxt, sx)
-        ref = unquantized_reference(np.ascontiguousarray(dy.T), np.ascontiguousarray(x.T))
-    else:
-        x, w = t["X"][:rows], t["W"]
-        qx, sx = quant_act_1x128(x, "cols")
-        qw, qwt, sw = quant_w_128x128(w)
-        got = gemm_fprop(qx, sx, qw, sw)
-        ref = unquantized_reference(x, w)
-        if key == "mlp_down_fprop_dgrad":
-            dy = t["dY"][:rows]
-            qdy, sdy = quant_act_1x128(dy, "cols")
-            got2 = gemm_dgrad(qdy, sdy, qwt, sw)
-            wt = np.ascontiguousarray(w.T)
-            ref2 = unquantized_reference(dy, wt)
-            assert np.linalg.norm(got2 - ref2) / np.linalg.norm(ref2) <= 0.05
-    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
-    assert rel <= 0.05, rel
+        r = rel(gemm_wgrad(qdyt, sdy, qxt, sx), unquantized_reference(np.ascontiguousarray(dy.T), np.ascontiguousarray(x.T)))
+        assert r <= 0.05, r
+        return
+    x, w = t["X"], t["W"]
+    qx, sx = quant_act_1x128(x, "cols")
+    qw, qwt, sw = quant_w_128x128(w)
+    r = rel(gemm_fprop(qx, sx, qw, sw), unquantized_reference(x, w))
+    assert r <= 0.05, r
+    if key == "mlp_down_fprop_dgrad":
+        dy = t["dY"]
+        qdy, sdy = quant_act_1x128(dy, "cols")
+        r2 = rel(gemm_dgrad(qdy, sdy, qwt, sw), unquantized_reference(dy, np.ascontiguousarray(w.T)))
+        assert r2 <= 0.05, r2
 
 
 def test_workload_generator_recipe():
@@ -229,3 +299,91 @@ def test_unquantized_reference_brute_force_and_closed_forms():
     two = unquantized_reference(f32_to_bf16_bits(np.array([[1.5, -2.0]], np.float32)),
                                 f32_to_bf16_bits(np.array([[0.25, 4.0], [3.0, 0.5]], np.float32)))
     assert two.tolist() == [[-7.625, 3.5]]
+
+
+# ---- accumulation contract (oracle.contract_allowance) ----
+# The allowance states what FP32 accumulation on a matrix unit with an 8-product fixed-point
+# window delivers: per group, products truncated toward zero to multiples of 2^(E-13) below the
+# group's largest product 2^E <= max|p| < 2^(E+1). The pins below check it against a scalar loop
+# and against a plain model of such an accumulator, including the model's worst case.
+
+def _window_model(a_row, b_row):
+    """Dot product as the windowed accumulator forms it: exact products, per group of 8 each
+    truncated toward zero to a multiple of 2^(E-13), group sums added in float32, then RNE to bf16
+    (as float64)."""
+    acc = np.float32(0.0)
+    for g in range(0, len(a_row), 8):
+        p = [Fraction(float(a_row[k])) * Fraction(float(b_row[k])) for k in range(g, g + 8)]
+        big = max(abs(x) for x in p)
+        if big == 0:
+            continue
+        e = big.numerator.bit_length() - big.denominator.bit_length()
+        if Fraction(2) ** e > big:
+            e -= 1
+        lsb = Fraction(2) ** (e - 13)
+        s = sum((abs(x) // lsb) * lsb * (1 if x >= 0 else -1) for x in p)
+        acc = np.float32(acc + np.float32(float(s)))
+    bits = int(bf16_round_from_f64(np.array([float(acc)]))[0])
+    return float(np.array([bits << 16], np.uint32).view(np.float32)[0])
+
+
+def test_contract_allowance_matches_a_scalar_loop():
+    rng = np.random.default_rng(41)
+    a = rng.standard_normal((3, 32)) * np.where(rng.random((3, 32)) < 0.1, 50.0, 1.0)
+    b = rng.standard_normal((4, 32))
+    ref = a @ b.T
+    got = contract_allowance(a, b, ref)
+    for i in range(3):
+        for j in range(4):
+            gmax = sum(max(abs(a[i, k] * b[j, k]) for k in range(g, g + 8)) for g in range(0, 32, 8))
+            asum = sum(abs(a[i, k] * b[j, k]) for k in range(32))
+            want = 2.0 ** -8 * abs(ref[i, j]) + (1 + 2.0 ** -8) * (7 * 2.0 ** -13 * gmax + 8 * 2.0 ** -24 * asum)
+            assert abs(got[i, j] - want) <= 1e-15 * want
+
+
+def test_contract_allowance_closed_form():
+    # one row: 448 at k = 0 and seven products of 2^-6 in the same group, zeros elsewhere (K = 128);
+    # sum_g max = 448, sum |p| = 448 + 7 * 2^-6, ref = 448 + 7 * 2^-6
+    a = np.zeros((1, 128))
+    a[0, 0] = 448.0
+    a[0, 1:8] = 2.0 ** -6
+    b = np.ones((1, 128))
+    ref = a @ b.T
+    want = 2.0 ** -8 * ref[0, 0] + (1 + 2.0 ** -8) * (7 * 2.0 ** -13 * 448 + 32 * 2.0 ** -24 * ref[0, 0])
+    assert contract_allowance(a, b, ref)[0, 0] == want
+    # the window model drops all seven small products (each below 2^(8-13) = 2^-5): error 7 * 2^-6,
+    # inside the allowance
+    model = _window_model(a[0], b[0])
+    assert model == 448.0 and abs(model - ref[0, 0]) <= want
+
+
+def test_contract_allowance_holds_for_the_window_model_and_is_nearly_tight():
+    # random operands with outliers in both, every element of the model inside the allowance
+    rng = np.random.default_rng(43)
+    vals = np.array([decode_e4m3(np.array([c], np.uint8))[0] for c in range(256) if (c & 0x7F) != 0x7F])
+    a = rng.choice(vals, size=(6, 64)) * np.where(rng.random((6, 64)) < 0.05, 16.0, 1.0)
+    b = rng.choice(vals, size=(5, 64))
+    ref = a @ b.T
+    allow = contract_allowance(a, b, ref)
+    model = np.array([[_window_model(a[i], b[j]) for j in range(5)] for i in range(6)])
+    assert contract_report(model, ref, allow)["violations"] == 0
+    # worst case of one group, no bf16 rounding: max product exactly 2^8, seven products just
+    # below the window's quantum 2^-5 (largest E4M3 value under 2^-5 is 0.029296875 = 15 * 2^-9)
+    a = np.zeros((1, 8))
+    a[0, 0] = 256.0
+    a[0, 1:] = 15 * 2.0 ** -9
+    b = np.ones((1, 8))
+    ref = a @ b.T
+    err = abs(_window_model(a[0], b[0]) - ref[0, 0])   # every small product is dropped
+    assert err == 7 * 15 * 2.0 ** -9
+    window_part = contract_allowance(a, b, ref)[0, 0] - 2.0 ** -8 * ref[0, 0]
+    assert err <= window_part and err / window_part > 0.9  # 6/7 of the allowance or more would fail a looser 2^-14
+
+
+def test_contract_report_counts_elements_outside_the_allowance():
+    ref = np.array([1.0, 2.0, 3.0, 4.0])
+    allow = np.array([0.5, 0.5, 0.5, 0.0])
+    gpu = np.array([1.5, 2.5000001, 2.5, 4.0])
+    rep = contract_report(gpu, ref, allow)
+    assert rep["violations"] == 1 and rep["n"] == 4
+    assert abs(rep["max_err_over_allowance"] - 0.5000001 / 0.5) < 1e-12
