@@ -5,13 +5,16 @@
 // and weight-gradient GEMMs take blockwise E4M3 operands; the product of the two block scales is
 // applied once per 128-wide K block and the result accumulates in FP32 and is written as BF16.
 //
-// Two kernels, one code path each (gfx950 only):
+// Three kernels, one code path each (gfx950 only):
 //  * gemm_mx_kernel (the default): 256 threads = 4 waves in a 2x2 grid own a BM x BN tile of D.
 //    Operands stream into a ring of five LDS stage buffers by direct-to-LDS buffer loads, and
 //    v_mfma_scale_f32_32x32x64_f8f6f4 applies the block scales while it accumulates in FP32: the
 //    scales are powers of two, so their exponent bytes are exact E8M0 scale operands (the gfx950
 //    counterpart of a block-scaled tensor-core path). The BF16 tile leaves through LDS as whole
 //    rows; an FP32 form writes (or adds to) an FP32 result. Details above the kernel.
+//  * gemm_mx_persistent_kernel: the same tiles and arithmetic, one workgroup per CU walking its
+//    tiles with a ring of stage buffers that runs across tile boundaries (taken when every CU
+//    gets two tiles or more, BF16 results, K a multiple of 256).
 //  * gemm_promote_kernel: register-staged, double-buffered LDS; one v_mfma_f32_16x16x128_f8f6f4
 //    covers a whole 128-wide scale block with a zero accumulator, and its FP32 partial is folded
 //    into the running accumulator with one FMA by sa*sb per element.
@@ -22,6 +25,7 @@
 #include "pf8_device.h"
 #include "pf8_launch.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace pf8 {
@@ -782,6 +786,405 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   }
 }
 
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)p));
+}
+
+// The persistent kernel's output staging buffer is written and read back through inline asm. The
+// compiler's wait insertion makes an LDS access that aliases none of the direct-to-LDS loads it
+// tracks wait for all of them, which here would be the next tile's first stages; the explicit
+// lgkmcnt waits and barriers around these accesses order them instead. The read waits for its
+// own results inside the asm statement before handing them over.
+__device__ __forceinline__ void stg_write8(uint32_t addr, uint32_t w0, uint32_t w1) {
+  asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(make_uint2(w0, w1)) : "memory");
+}
+
+__device__ __forceinline__ void stg_read8x16(const uint32_t (&addr)[8], v4i (&v)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n"
+      "ds_read_b128 %1, %9\n"
+      "ds_read_b128 %2, %10\n"
+      "ds_read_b128 %3, %11\n"
+      "ds_read_b128 %4, %12\n"
+      "ds_read_b128 %5, %13\n"
+      "ds_read_b128 %6, %14\n"
+      "ds_read_b128 %7, %15\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]), "v"(addr[7])
+      : "memory");
+}
+
+// =============================================================================================
+// Persistent MX kernel: one workgroup per CU walks a fixed list of BM x 256 output tiles
+// (BM = 256 or 192), BF16 result, M and N multiples of the tile, K a multiple of 256 (>= 512).
+//
+//  * The workgroup with id w runs on XCD w mod 8 and takes every (grid/8)-th tile of that XCD's
+//    contiguous tile range, i.e. the same tiles, in the same order, as the one-tile-per-workgroup
+//    kernel's rounds; its workgroups never wait for one another.
+//  * K streams in 64-byte stages through a ring of four LDS buffers that runs on across tile
+//    boundaries: the refills of a tile's last four stages fetch the next tile's first four (all
+//    of them issued before the tile's output stores), so the next tile's operands arrive while the
+//    result leaves, and no workgroup start or prologue separates the tiles. The last tile fetches
+//    its own first stages again, so that every tile runs the same code; the kernel drains them.
+//  * Stage s of every tile sits in buffer s mod 4 (K is a multiple of 256): buffer indices and
+//    stage parities are compile-time constants of the position in a four-stage loop body. The
+//    two stages of a 128-wide K block share one set of scale registers, loaded with the even one.
+//  * The result leaves through a fifth LDS buffer of its own, one 64-row slab at a time: each
+//    wave writes 32 rows of its accumulators as BF16, then every thread moves whole 16-byte
+//    chunks of whole rows with non-temporal stores.
+//  * The waits count loads exactly as in gemm_mx_kernel. The first three waits of a tile also
+//    count the previous tile's stores, which were issued after the stages they wait for: loads
+//    and stores complete in issue order, so those waits do not wait for the stores.
+//  * The tile loop is rotated (tile 0's first stages come before it, every trip ends with the next
+//    tile's first stages), so each wait has one compile-time count. Lane-dependent offsets are
+//    recomputed at the top of every tile from an opaque copy of the thread id: hoisted out of the
+//    tile loop, their many derived addresses would stay live and spill.
+// Results are bitwise those of gemm_mx_kernel with the same tile: every output element sums the
+// same products in the same order.
+template <int BM, bool ROW_B>
+__global__ __launch_bounds__(256) void gemm_mx_persistent_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+  constexpr int BN = 256, BK = 64, NST = 4;
+  static_assert(BM == 256 || BM == 192, "256 or 192 output rows per tile");
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int A_ST = BM * BK, ST = (BM + BN) * BK;
+  constexpr int A_DMA = BM / 64, B_DMA = BN / 64, D = A_DMA + B_DMA;
+  constexpr int SB = ROW_B ? TN : 1;  // tile scales: a wave's 128 columns lie in one 128-column tile
+  constexpr int SS = TM + SB;         // scale loads of an even stage
+  constexpr int RP = BN * 2;          // staged output row pitch (bytes)
+  constexpr int CH = BN / 8;          // 16-byte chunks per output row
+  constexpr int ST_STORES = (64 * RP) / (256 * 16);  // 16-byte stores per thread and 64-row slab
+  constexpr int N_STORES = TM * ST_STORES;           // per thread and tile
+  static_assert(ST_STORES == 8, "eight 16-byte chunks per thread and slab");
+  __shared__ __align__(16) uint8_t buf0[ST];
+  __shared__ __align__(16) uint8_t buf1[ST];
+  __shared__ __align__(16) uint8_t buf2[ST];
+  __shared__ __align__(16) uint8_t buf3[ST];
+  __shared__ __align__(16) uint8_t stg[64 * RP];
+
+  const int t0 = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t0 >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ns = static_cast<int>(p.k / BK);  // a multiple of 4, >= 8 (the launcher checks)
+
+  // ---- this workgroup's tiles ----
+  const int nb = tiles_m * tiles_n;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, slots = gridDim.x >> 3;
+  const int q = nb >> 3, rem = nb & 7;
+  const int xcd_tiles = q + (xcd < rem ? 1 : 0), xcd_base = xcd * q + min(xcd, rem);
+  const int ntiles = slot < xcd_tiles ? (xcd_tiles - slot + slots - 1) / slots : 0;
+  if (ntiles == 0) return;
+  auto tile_origin = [&](int r, int64_t& m0, int64_t& n0) {
+    const int bid = xcd_base + slot + slots * r;
+    constexpr int kGroupM = 8;
+    const int per_group = kGroupM * tiles_n;
+    const int grp = bid / per_group;
+    const int first_m = grp * kGroupM;
+    const int gsize = min(tiles_m - first_m, kGroupM);
+    const int in_grp = bid - grp * per_group;
+    const int tm = __builtin_amdgcn_readfirstlane(first_m + in_grp % gsize);
+    const int tn = __builtin_amdgcn_readfirstlane(in_grp / gsize);
+    m0 = static_cast<int64_t>(tm) * BM;
+    n0 = static_cast<int64_t>(tn) * BN;
+  };
+  auto bufs = [&](int u) -> uint8_t* { return u == 0 ? buf0 : u == 1 ? buf1 : u == 2 ? buf2 : buf3; };
+
+  // ---- lane offsets (recomputed per tile) ----
+  int t = t0, lane = t0 & 63;
+  int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
+  int voff_a = 0, voff_b = 0, l32 = 0, half = 0, fo0 = 0, fo1 = 0;
+  auto refresh = [&]() {
+    asm volatile("" : "+v"(t));
+    asm volatile("" : "+s"(lda), "+s"(ldb));
+    lane = t & 63;
+    const int dma_row = lane >> 2;
+    const int dma_chunk = (lane & 3) ^ ((dma_row >> 2) & 3);
+    voff_a = dma_row * lda + dma_chunk * 16;
+    voff_b = dma_row * ldb + dma_chunk * 16;
+    l32 = lane & 31;
+    half = lane >> 5;
+    const int sw = (l32 >> 2) & 3;
+    fo0 = l32 * BK + (((2 * half) ^ sw) << 4);
+    fo1 = l32 * BK + (((2 * half + 1) ^ sw) << 4);
+  };
+  refresh();
+
+  // ---- load state: the tile whose stages the refills fetch ----
+  __amdgpu_buffer_rsrc_t rsrc_a, rsrc_b;
+  int64_t a_row[TM], b_row[SB];
+  auto set_load_tile = [&](int r) {
+    int64_t m0, n0;
+    tile_origin(r, m0, n0);
+    rsrc_a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.a + m0 * p.lda), 0, BM * lda, kBufferFlags);
+    rsrc_b = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.b + n0 * p.ldb), 0, BN * ldb, kBufferFlags);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a_row[i] = m0 + wm * WM + 32 * i + l32;
+#pragma unroll
+    for (int j = 0; j < SB; ++j) b_row[j] = n0 + wn * WN + 32 * j + l32;
+  };
+  // scale registers: one set per even buffer (0 and 2); an odd stage reads the previous buffer's
+  uint32_t sc_a[2][TM], sc_b[2][SB];
+  auto load_scales = [&](int s, uint32_t (&sa)[TM], uint32_t (&sb)[SB]) {
+    // the waits count exactly TM + SB loads here: opaque indices keep the compiler from merging
+    // two of them or hoisting one above earlier loads (as in gemm_mx_kernel)
+    const int64_t kb = s >> 1;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      int64_t idx = kb * p.ld_as + a_row[i];
+      asm volatile("" : "+v"(idx));
+      sa[i] = __float_as_uint(p.a_dscale[idx]);
+    }
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      int64_t idx = ROW_B ? kb * p.sb_k + b_row[j] * p.sb_n : (b_row[j] >> 7) * p.sb_n + kb * p.sb_k;
+      asm volatile("" : "+v"(idx));
+      sb[j] = __float_as_uint(p.b_dscale[idx]);
+    }
+  };
+  // loads of the load tile's stage s into buffer u = s mod 4: part 0 = the A operand, part 1 = the
+  // scales (even stages) and the B operand
+  auto issue_part = [&](auto u_c, int s, auto part_c) {
+    constexpr int u = decltype(u_c)::value;
+    constexpr int part = decltype(part_c)::value;
+    uint8_t* buf = bufs(u);
+    if constexpr (part == 1 && (u % 2 == 0)) load_scales(s, sc_a[u / 2], sc_b[u / 2]);
+    const int kofs = s * BK;
+#pragma unroll
+    for (int j = 0; j < (part == 0 ? A_DMA : 0); ++j) {
+      const int slab = wave + 4 * j;
+      auto* dst = (__attribute__((address_space(3))) void*)(buf + slab * 16 * BK);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, dst, 16, voff_a, slab * 16 * lda + kofs, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < (part == 1 ? B_DMA : 0); ++j) {
+      const int slab = wave + 4 * j;
+      auto* dst = (__attribute__((address_space(3))) void*)(buf + A_ST + slab * 16 * BK);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, dst, 16, voff_b, slab * 16 * ldb + kofs, 0, 0);
+    }
+  };
+  using PA = std::integral_constant<int, 0>;
+  using PB = std::integral_constant<int, 1>;
+
+  // ---- operand fragments: set f = stage parity ----
+  v8i fa[2][TM], fb[2][TN];
+  auto read_frags = [&](const uint8_t* buf, v8i (&a)[TM], v8i (&b)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = lds_read32(buf, (wm * WM + 32 * i) * BK + fo0, (wm * WM + 32 * i) * BK + fo1);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      b[j] = lds_read32(buf, A_ST + (wn * WN + 32 * j) * BK + fo0, A_ST + (wn * WN + 32 * j) * BK + fo1);
+  };
+
+  v16f acc[TM][TN];
+
+#define PF8_WAIT_VM_LGKM0(n0)                                                                  \
+  do {                                                                                         \
+    constexpr int n_ = (n0) < 63 ? (n0) : 63;                                                  \
+    __builtin_amdgcn_s_waitcnt((n_ & 0xF) | ((n_ >> 4) << 14) | (0x7 << 4) | (0x0 << 8));      \
+  } while (0)
+
+  // One stage at body position u (tile stage s with s mod 4 = u):
+  //  PREV: the first half sends the scales and B loads of load-tile stage ps (into buffer u - 1)
+  //  REFILL: the second half sends the A loads of load-tile stage rs (into buffer u); EARLYB: and
+  //          its B loads too (a tile's last stage: the next tile's stage 3 then leaves before the
+  //          output stores)
+  //  SWITCH: before the refill the load tile becomes tile `next`
+  //  ZERO: the tile's first stage: the MFMAs start from zero
+  //  INF: stages issued after stage s + 1 that may still be in flight at the wait
+  //  XTRA: vector-memory operations issued after stage s + 1 besides those stages (the previous
+  //        tile's output stores)
+  auto stage = [&](auto u_c, auto prev_c, int ps, auto refill_c, int rs, auto earlyb_c, auto switch_c, int next,
+                   auto zero_c, auto inf_c, auto xtra_c) {
+    constexpr int u = decltype(u_c)::value;
+    constexpr bool prev = decltype(prev_c)::value, refill = decltype(refill_c)::value;
+    constexpr bool earlyb = decltype(earlyb_c)::value, sw_tile = decltype(switch_c)::value;
+    constexpr bool zero = decltype(zero_c)::value;
+    constexpr int inf = decltype(inf_c)::value, xtra = decltype(xtra_c)::value;
+    constexpr int f = u & 1, un = (u + 1) & 3, fn = un & 1;
+    constexpr bool odd = (u & 1) != 0;
+    constexpr int us = u / 2;  // this K block's scale registers (loaded with its even stage)
+    int sae[TM], sbe[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      uint32_t v = sc_a[us][i];
+      asm volatile("" : "+v"(v));
+      sae[i] = static_cast<int>(v >> 23);
+    }
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      uint32_t v = sc_b[us][j];
+      asm volatile("" : "+v"(v));
+      sbe[j] = static_cast<int>(v >> 23);
+    }
+#pragma unroll
+    for (int j = SB; j < TN; ++j) sbe[j] = sbe[0];
+    auto mfma_rows = [&](int i0, int i1) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if (i < i0 || i >= i1) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const v16f c = zero ? v16f{} : acc[i][j];
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[f][j], fa[f][i], c, 0, 0, 0, sbe[j], 0, sae[i]);
+        }
+      }
+    };
+    // the stage PREV sends lives in buffer u - 1 and has the other parity
+    if constexpr (prev) issue_part(std::integral_constant<int, (u + 3) & 3>{}, ps, PB{});
+    mfma_rows(0, TM / 2);
+    if constexpr (prev) interleave_groups<(TM / 2) * TN, B_DMA + (odd ? SS : 0), 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    // stage s + 2 has this stage's parity, stage s + 3 the other
+    constexpr int after = (inf >= 1 ? D + (odd ? 0 : SS) : 0) + (inf >= 2 ? D + (odd ? SS : 0) : 0);
+    PF8_WAIT_VM_LGKM0(after + xtra);
+    __builtin_amdgcn_s_barrier();
+    if constexpr (sw_tile) set_load_tile(next);
+    if constexpr (refill) issue_part(u_c, rs, PA{});
+    if constexpr (earlyb) issue_part(u_c, rs, PB{});
+    read_frags(bufs(un), fa[fn], fb[fn]);
+    mfma_rows(TM / 2, TM);
+    interleave_groups<(TM - TM / 2) * TN, (refill ? A_DMA : 0) + (earlyb ? B_DMA : 0), 2 * (TM + TN)>();
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using F = std::false_type;
+  using T = std::true_type;
+  using XS = std::integral_constant<int, N_STORES>;
+
+  // ---- prologue: tile 0's stages 0..3 ----
+  set_load_tile(0);
+  issue_part(I0{}, 0, PA{});
+  issue_part(I0{}, 0, PB{});
+  __builtin_amdgcn_sched_barrier(0);
+  issue_part(I1{}, 1, PA{});
+  issue_part(I1{}, 1, PB{});
+  __builtin_amdgcn_sched_barrier(0);
+  issue_part(I2{}, 2, PA{});
+  issue_part(I2{}, 2, PB{});
+  __builtin_amdgcn_sched_barrier(0);
+  issue_part(I3{}, 3, PA{});
+  issue_part(I3{}, 3, PB{});
+  __builtin_amdgcn_sched_barrier(0);
+  PF8_WAIT_VM_LGKM0(D + (D + SS) + D);  // after stage 0: stages 1, 2 and 3
+  __builtin_amdgcn_s_barrier();
+  read_frags(buf0, fa[0], fb[0]);
+
+  // tile 0's first body (no stores before it)
+  stage(I0{}, F{}, 0, T{}, 4, F{}, F{}, 0, T{}, I2{}, I0{});
+  stage(I1{}, T{}, 4, T{}, 5, F{}, F{}, 0, F{}, I2{}, I0{});
+  stage(I2{}, T{}, 5, T{}, 6, F{}, F{}, 0, F{}, I2{}, I0{});
+  stage(I3{}, T{}, 6, T{}, 7, F{}, F{}, 0, F{}, I2{}, I0{});
+  for (int r = 0;; ++r) {
+    refresh();
+    int s = 4;
+    for (; s < ns - 4; s += 4) {
+      stage(I0{}, T{}, s + 3, T{}, s + 4, F{}, F{}, 0, F{}, I2{}, I0{});
+      stage(I1{}, T{}, s + 4, T{}, s + 5, F{}, F{}, 0, F{}, I2{}, I0{});
+      stage(I2{}, T{}, s + 5, T{}, s + 6, F{}, F{}, 0, F{}, I2{}, I0{});
+      stage(I3{}, T{}, s + 6, T{}, s + 7, F{}, F{}, 0, F{}, I2{}, I0{});
+    }
+    // last body: its refills fetch the next tile's stages 0..3
+    const int next = r + 1 < ntiles ? r + 1 : r;
+    stage(I0{}, T{}, s + 3, T{}, 0, F{}, T{}, next, F{}, I2{}, I0{});
+    stage(I1{}, T{}, 0, T{}, 1, F{}, F{}, 0, F{}, I2{}, I0{});
+    stage(I2{}, T{}, 1, T{}, 2, F{}, F{}, 0, F{}, I2{}, I0{});
+    stage(I3{}, T{}, 2, T{}, 3, T{}, F{}, 0, F{}, I2{}, I0{});
+
+    // ---- epilogue: slab i holds rows wm*WM + 32i + (lane % 32) of both wave rows, staged as row
+    // sr = wm*32 + lane%32; chunk c of staged row sr sits at chunk c ^ (sr mod 32) ----
+    int64_t m0, n0;
+    tile_origin(r, m0, n0);
+    auto phys = [](int row, int c) -> int { return c ^ (row & (CH - 1)); };
+    constexpr int kWaitLgkm = 0xF | (0x7 << 4) | (0x3 << 14);  // lgkmcnt(0) only
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      {
+        const int sr = wm * 32 + l32;
+        const uint32_t rb = lds_addr(stg) + sr * RP;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int c = (wn * WN + 32 * j + 8 * q4) >> 3;
+            const uint32_t w0 = pack_bf16x2(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1]);
+            const uint32_t w1 = pack_bf16x2(acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]);
+            stg_write8(rb + phys(sr, c) * 16 + 8 * half, w0, w1);
+          }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+      __builtin_amdgcn_s_barrier();
+      uint32_t ra[ST_STORES];
+      v4i rv[ST_STORES];
+#pragma unroll
+      for (int it = 0; it < ST_STORES; ++it) {
+        const int qq = t + 256 * it;
+        const int row = qq / CH, c = qq % CH;
+        ra[it] = lds_addr(stg) + row * RP + phys(row, c) * 16;
+      }
+      stg_read8x16(ra, rv);
+#pragma unroll
+      for (int it = 0; it < ST_STORES; ++it) {
+        const int qq = t + 256 * it;
+        const int row = qq / CH, c = qq % CH;
+        const int64_t gm = m0 + (row >> 5) * WM + 32 * i + (row & 31), gn = n0 + 8 * c;
+        __builtin_nontemporal_store(rv[it], reinterpret_cast<v4i*>(p.d + gm * p.ldd + gn));
+      }
+      if (i + 1 < TM) {
+        // every wave has read this slab back before the next one is staged
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+        __builtin_amdgcn_s_barrier();
+      }
+    }
+    if (r + 1 == ntiles) break;
+    // the next tile's first body: all of its stage 3 came with the last refills (no PREV in
+    // stage 0), and this tile's stores follow stages 1..3
+    stage(I0{}, F{}, 0, T{}, 4, F{}, F{}, 0, T{}, I2{}, XS{});
+    stage(I1{}, T{}, 4, T{}, 5, F{}, F{}, 0, F{}, I2{}, XS{});
+    stage(I2{}, T{}, 5, T{}, 6, F{}, F{}, 0, F{}, I2{}, XS{});
+    stage(I3{}, T{}, 6, T{}, 7, F{}, F{}, 0, F{}, I2{}, I0{});
+  }
+  // the last tile's extra fetch writes LDS: it lands before the workgroup ends
+  __builtin_amdgcn_s_waitcnt(0);
+#undef PF8_WAIT_VM_LGKM0
+}
+
+// CUs of the current device (cached per device).
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// Launches the persistent kernel for BM x 256 tiles when it applies: a BF16 result, tiles that
+// divide M and N, K a multiple of 256 with at least 8 stages, and at least two tiles per CU.
+// Returns hipErrorNotSupported (nothing launched) otherwise.
+template <int BM>
+static hipError_t launch_persistent(const GemmArgs& args, bool row_b, hipStream_t stream) {
+  if (args.d32 != nullptr || args.m % BM != 0 || args.n % 256 != 0 || args.k % 256 != 0 || args.k < 512)
+    return hipErrorNotSupported;
+  const int64_t tiles_m = args.m / BM, tiles_n = args.n / 256;
+  const int grid = device_cus() / 8 * 8;
+  if (grid < 8 || tiles_m * tiles_n < 2 * static_cast<int64_t>(grid)) return hipErrorNotSupported;
+  const int tm = static_cast<int>(tiles_m), tn = static_cast<int>(tiles_n);
+  if (row_b)
+    hipLaunchKernelGGL((gemm_mx_persistent_kernel<BM, true>), dim3(grid), dim3(256), 0, stream, args, tm, tn);
+  else
+    hipLaunchKernelGGL((gemm_mx_persistent_kernel<BM, false>), dim3(grid), dim3(256), 0, stream, args, tm, tn);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, bool ROW_B, bool MX>
 static hipError_t launch_tile(const GemmArgs& args, hipStream_t stream) {
   const int tiles_m = static_cast<int>((args.m + BM - 1) / BM);
@@ -882,6 +1285,13 @@ hipError_t launch_gemm(const GemmArgs& args, bool row_b_scale, bool mx, hipStrea
       best = i;
       best_cost = cost;
     }
+  }
+  // two tiles or more per CU: the persistent kernel overlaps each tile's output with the next
+  // tile's first loads
+  if (best == 0 || best == 2) {
+    const hipError_t e = best == 0 ? launch_persistent<256>(args, row_b_scale, stream)
+                                   : launch_persistent<192>(args, row_b_scale, stream);
+    if (e != hipErrorNotSupported) return e;
   }
   switch (best) {
     case 0: return launch_tile<256, 256, true>(args, row_b_scale, stream);

@@ -131,3 +131,54 @@ def test_whole_kernel_load_totals_match_the_stage_layout(asm):
             assert scale == want_scale, f"{name}: {scale} scale loads, expected {want_scale}"
         checked += 1
     assert checked >= 40, checked
+
+
+def _inner_loops(body):
+    """Natural loops whose header label is followed (on its line or the next) by a 'Loop Header'
+    comment and which contain no other loop header."""
+    out = []
+    for i, line in enumerate(body):
+        m = re.match(r"^(\.LBB\d+_\d+):", line)
+        if not m or not any("Loop Header" in ln for ln in body[i:i + 2]):
+            continue
+        for j in range(i + 1, len(body)):
+            if re.search(r"s_cbranch_\w+\s+" + re.escape(m.group(1)) + r"\s*$", body[j]):
+                inner = body[i + 2:j]
+                if not any("Loop Header" in ln for ln in inner):
+                    out.append(body[i:j + 1])
+                break
+    return out
+
+
+def test_persistent_kernel_load_counts(asm):
+    """The persistent kernel's waits count its loads per stage and the output stores per tile.
+
+    Over the whole kernel: the prologue's four stages (4 D direct-to-LDS loads, scales of stages 0
+    and 2), tile 0's first body, the K loop body, the last body and the next tile's first body
+    (4 A + 3 B, 4 D, 4 A + 5 B and 4 A + 3 B loads; two scale sets each), i.e. 20 A_DMA + 19 B_DMA
+    direct-to-LDS loads and 10 scale sets; 8 stores per thread and 64-row slab. The K loop's trip
+    holds four stages: 4 D loads and two scale sets."""
+    kern = re.compile(r"_ZN3pf825gemm_mx_persistent_kernelILi(\d+)ELb(\d)E")
+    checked = 0
+    for name, body in _functions(asm).items():
+        m = kern.match(name)
+        if not m:
+            continue
+        bm, row_b = int(m.group(1)), int(m.group(2))
+        a_dma, b_dma, tm = bm // 64, 4, bm // 64
+        ss = tm + (4 if row_b else 1)
+        lds = sum(1 for ln in body if ln.strip().startswith("buffer_load_dword") and " lds" in ln)
+        scale = sum(1 for ln in body if ln.strip().startswith("global_load_dword "))
+        stores = sum(1 for ln in body if ln.strip().startswith("global_store"))
+        assert lds == 20 * a_dma + 19 * b_dma, f"{name}: {lds} direct-to-LDS loads"
+        assert scale == 10 * ss, f"{name}: {scale} scale loads"
+        assert stores == 8 * tm, f"{name}: {stores} stores"
+        loops = _inner_loops(body)
+        assert loops, name
+        for lp in loops:
+            n_lds = sum(1 for ln in lp if ln.strip().startswith("buffer_load_dword") and " lds" in ln)
+            n_sc = sum(1 for ln in lp if ln.strip().startswith("global_load_dword "))
+            n_st = sum(1 for ln in lp if ln.strip().startswith("global_store"))
+            assert (n_lds, n_sc, n_st) == (4 * (a_dma + b_dma), 2 * ss, 0), f"{name}: loop trip {n_lds}, {n_sc}, {n_st}"
+        checked += 1
+    assert checked == 4, checked

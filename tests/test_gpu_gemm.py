@@ -710,3 +710,95 @@ def test_full_size_bf16_and_f32_gemms_sampled():
     got = base.cpu().numpy()[cols].astype(np.float64)
     rep = oracle.gemm_tolerance_report(got, ref)
     assert rep["violations"] == 0, rep
+
+
+# ---- persistent kernel: shapes with two tiles or more per CU, K a multiple of 256 ----
+# (M, N, K) per layout; each takes the persistent kernel: 256x256 tiles (four, two and a half, and
+# 2.1 per CU with a tile count that is not a multiple of 8) and 192x256 tiles.
+PERSISTENT = [("fprop", 4096, 16384, 512), ("dgrad", 5120, 8192, 768), ("fprop", 5120, 6912, 512),
+              ("wgrad", 12288, 2048, 1024), ("wgrad", 8192, 4096, 1024), ("fprop", 6144, 12288, 1024)]
+
+
+@pytest.mark.parametrize("lname,m,n,k", PERSISTENT, ids=lambda v: str(v))
+def test_persistent_kernel_matches_one_tile_kernel_and_oracle(lname, m, n, k):
+    """The persistent kernel sums every element's products in the one-tile kernel's order: its BF16
+    result equals the rounded result of the FP32 kernel (one tile per workgroup, same tile shape)
+    bit for bit; sampled rows, the first and last included, meet the oracle's bar."""
+    layout = LAYOUTS[lname]
+    qa, sa, qb, sb, sb_n, sb_k, _ = _operands_nosample(layout, m, n, k, m + n + k)
+    a, sa_d, b, sb_d = to_dev_u8(qa), to_dev_f32(sa), to_dev_u8(qb), to_dev_f32(sb)
+    d16 = pf8.block_gemm(layout, a, sa_d, b, sb_d, sb_n, sb_k)
+    d32 = pf8.block_gemm_f32(layout, a, sa_d, b, sb_d, sb_n, sb_k)
+    torch.cuda.synchronize()
+    assert torch.equal(d32.to(torch.bfloat16).view(torch.int16), d16.view(torch.int16))
+    rows = np.unique(np.concatenate([[0, m - 1], _sample_rows(m, 48, m + k)]))
+    got = bf16_f64(d16[torch.from_numpy(rows).to(DEV)])
+    _report(got, _ref_rows(layout, qa, sa, qb, sb, rows), f"{lname} {m}x{n}x{k}")
+
+
+def _operands_nosample(layout, m, n, k, seed):
+    """Workload-distributed codes for one layout (activations with outliers, weights and
+    gradients Gaussian), as (a, sa, b, sb, sb_n, sb_k, None)."""
+    if layout == pf8.PF8_WGRAD:
+        qa, sa = oracle.quant_act_1x128(_rand_bits((k, m), seed, 1e-3, outliers=False), "rows")
+        qb, sb = oracle.quant_act_1x128(_rand_bits((k, n), seed + 1), "rows")
+        return qa, sa, qb, sb, 1, sb.shape[1], None
+    if layout == pf8.PF8_FPROP:
+        qa, sa = oracle.quant_act_1x128(_rand_bits((m, k), seed), "cols")
+        qw, _, sw = oracle.quant_w_128x128(_rand_bits((n, k), seed + 1, 0.02, outliers=False))
+        return qa, sa, qw, sw, sw.shape[1], 1, None
+    qa, sa = oracle.quant_act_1x128(_rand_bits((m, k), seed, 1e-3, outliers=False), "cols")
+    _, qwt, sw = oracle.quant_w_128x128(_rand_bits((k, n), seed + 1, 0.01, outliers=False))
+    return qa, sa, qwt, sw, 1, sw.shape[1], None
+
+
+def _ref_rows(layout, qa, sa, qb, sb, rows):
+    if layout == pf8.PF8_FPROP:
+        return oracle.gemm_fprop(qa[rows], sa[:, rows], qb, sb)
+    if layout == pf8.PF8_DGRAD:
+        return oracle.gemm_dgrad(qa[rows], sa[:, rows], qb, sb)
+    return oracle.gemm_wgrad(qa[rows], sa[:, rows], qb, sb)
+
+
+@pytest.mark.parametrize("lname,m,n,k", [("dgrad", 4096, 8192, 512), ("wgrad", 12288, 2048, 512)], ids=lambda v: str(v))
+def test_persistent_kernel_arbitrary_codes_within_contract(lname, m, n, k):
+    """Arbitrary E4M3 codes in both operands and power-of-two scales per block through the persistent
+    kernel (256x256 and 192x256 tiles): sampled rows inside the accumulation contract, and the same
+    bits as the FP32 kernel rounded."""
+    layout = LAYOUTS[lname]
+    rng = np.random.default_rng(m + n + k)
+    qa, qb = _codes(rng, (m, k)), _codes(rng, (n, k))
+    pow2 = lambda *sh: np.ldexp(1.0, rng.integers(-6, 7, size=sh)).astype(np.float32)  # noqa: E731
+    sa = pow2(k // 128, m)
+    if layout == pf8.PF8_DGRAD:
+        sb, sb_n, sb_k = pow2(k // 128, n // 128), 1, n // 128
+        deq_b = oracle.dequant_w_tiles(qb, sb.T)
+    else:
+        sb, sb_n, sb_k = pow2(k // 128, n), 1, n
+        deq_b = oracle.dequant_act_groups(qb, sb)
+    a, sa_d, b, sb_d = to_dev_u8(qa), to_dev_f32(sa), to_dev_u8(qb), to_dev_f32(sb)
+    d16 = pf8.block_gemm(layout, a, sa_d, b, sb_d, sb_n, sb_k)
+    d32 = pf8.block_gemm_f32(layout, a, sa_d, b, sb_d, sb_n, sb_k)
+    torch.cuda.synchronize()
+    assert torch.equal(d32.to(torch.bfloat16).view(torch.int16), d16.view(torch.int16))
+    rows = np.unique(np.concatenate([[0, m - 1], _sample_rows(m, 32, k)]))
+    got = bf16_f64(d16[torch.from_numpy(rows).to(DEV)])
+    _contract(got, _ref_rows(layout, qa, sa, qb, sb, rows), oracle.dequant_act_groups(qa[rows], sa[:, rows]), deq_b,
+              f"{lname} {m}x{n}x{k}")
+
+
+def test_persistent_kernel_repeats_bitwise_between_other_launches():
+    """Twenty launches of the persistent kernel, each after other GEMM and quantiser launches that
+    reuse the caches and the CUs, give the same bits every time (a wait that counted too few loads
+    would read stale LDS operands now and then)."""
+    m, n, k = 4096, 8192, 1024
+    qa, sa, qb, sb, sb_n, sb_k, _ = _operands_nosample(pf8.PF8_FPROP, m, n, k, 7)
+    a, sa_d, b, sb_d = to_dev_u8(qa), to_dev_f32(sa), to_dev_u8(qb), to_dev_f32(sb)
+    first = pf8.block_gemm(pf8.PF8_FPROP, a, sa_d, b, sb_d, sb_n, sb_k)
+    other_x = to_dev_bf16(_rand_bits((1024, 2048), 8))
+    for i in range(20):
+        pf8.quant_act_1x128(other_x, "cols")
+        pf8.block_gemm(pf8.PF8_FPROP, a[:1000], sa_d, b[:700], sb_d, sb_n, sb_k)  # ragged: one-tile kernel
+        again = pf8.block_gemm(pf8.PF8_FPROP, a, sa_d, b, sb_d, sb_n, sb_k)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int16), first.view(torch.int16)), f"launch {i}"
