@@ -12,6 +12,15 @@ namespace {
 constexpr int64_t kGroup = 128;
 constexpr int64_t kMaxTilePitch = ((int64_t{1} << 31) - 1) / 256;  // 256 rows x pitch must fit a signed 32-bit offset
 
+// Every dimension, leading dimension and scale stride is at most 2^31 - 1 (PF8_ESHAPE otherwise):
+// no array that large fits a GPU's memory, and the bound keeps every size product and pitch in
+// bytes below 2^63, so the checks below cannot overflow.
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+template <typename... T>
+bool any_too_big(T... v) {
+  return ((v > kMaxDim) || ...);
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
@@ -49,6 +58,7 @@ pf8_status pf8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_
   if (x == nullptr || q == nullptr || dscale == nullptr) return PF8_EINVAL;
   if (axis != PF8_ALONG_COLS && axis != PF8_ALONG_ROWS) return PF8_EINVAL;
   if (rows <= 0 || cols <= 0) return PF8_EINVAL;
+  if (any_too_big(rows, cols, ldx, ldq, ld_s)) return PF8_ESHAPE;
   if (ldx < cols) return PF8_EINVAL;
   if (axis == PF8_ALONG_COLS) {
     if (cols % kGroup != 0) return PF8_ESHAPE;
@@ -73,6 +83,7 @@ pf8_status pf8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t
   if (x == nullptr || q_row == nullptr || dscale_row == nullptr || q_col == nullptr || dscale_col == nullptr)
     return PF8_EINVAL;
   if (rows <= 0 || cols <= 0) return PF8_EINVAL;
+  if (any_too_big(rows, cols, ldx, ldq_row, ld_sr, ldq_col, ld_sc)) return PF8_ESHAPE;
   if (rows % kGroup != 0 || cols % kGroup != 0) return PF8_ESHAPE;
   if (ldx < cols || ldq_row < cols || ld_sr < rows || ldq_col < rows || ld_sc < cols) return PF8_EINVAL;
   if (!aligned16(x) || !aligned16(q_row) || !aligned16(q_col) || !aligned4(dscale_row) || !aligned4(dscale_col))
@@ -91,6 +102,8 @@ pf8_status pf8_quant_fwd(const void* x, int64_t m, int64_t k, int64_t ldx, void*
       qw == nullptr || sw == nullptr)
     return PF8_EINVAL;
   if (m <= 0 || n <= 0 || k <= 0) return PF8_EINVAL;
+  if (any_too_big(m, n, k, ldx, ldqx, ld_sx, ldqxt, ld_sxt, ldw, ldqw, ld_sw, qwt != nullptr ? ldqwt : 0))
+    return PF8_ESHAPE;
   if (m % kGroup != 0 || n % kGroup != 0 || k % kGroup != 0) return PF8_ESHAPE;
   if (ldx < k || ldqx < k || ld_sx < m || ldqxt < m || ld_sxt < k) return PF8_EINVAL;
   if (ldw < k || ldqw < k || ld_sw < k / kGroup || (qwt != nullptr && ldqwt < n)) return PF8_EINVAL;
@@ -109,6 +122,7 @@ pf8_status pf8_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw,
                         float* dscale, int64_t ld_s, void* hip_stream) {
   if (w == nullptr || q == nullptr || dscale == nullptr) return PF8_EINVAL;
   if (n <= 0 || k <= 0) return PF8_EINVAL;
+  if (any_too_big(n, k, ldw, ldq, ld_s, qt != nullptr ? ldqt : 0)) return PF8_ESHAPE;
   if (n % kGroup != 0 || k % kGroup != 0) return PF8_ESHAPE;
   if (ldw < k || ldq < k || ld_s < k / kGroup || (qt != nullptr && ldqt < n)) return PF8_EINVAL;
   if (!aligned16(w) || !aligned16(q) || !aligned4(dscale) || (ldw * 2) % 16 != 0 || ldq % 16 != 0) return PF8_EALIGN;
@@ -126,6 +140,7 @@ pf8_status pf8_block_gemm_variant(int variant, pf8_layout layout, int64_t m, int
   if (layout != PF8_FPROP && layout != PF8_DGRAD && layout != PF8_WGRAD) return PF8_EINVAL;
   if (a == nullptr || b == nullptr || d == nullptr || a_dscale == nullptr || b_dscale == nullptr) return PF8_EINVAL;
   if (m <= 0 || n <= 0 || k <= 0) return PF8_EINVAL;
+  if (any_too_big(m, n, k, lda, ldb, ldd, ld_as, sb_n, sb_k)) return PF8_ESHAPE;
   if (k % kGroup != 0) return PF8_ESHAPE;
   if (lda < k || ldb < k || ldd < n || ld_as < m || sb_n < 1 || sb_k < 1) return PF8_EINVAL;
   if (!aligned16(a) || !aligned16(b) || !aligned16(d) || !aligned4(a_dscale) || !aligned4(b_dscale)) return PF8_EALIGN;
@@ -146,6 +161,7 @@ pf8_status pf8_block_gemm_f32(pf8_layout layout, int64_t m, int64_t n, int64_t k
   if (accumulate != 0 && accumulate != 1) return PF8_EINVAL;
   if (a == nullptr || b == nullptr || d == nullptr || a_dscale == nullptr || b_dscale == nullptr) return PF8_EINVAL;
   if (m <= 0 || n <= 0 || k <= 0) return PF8_EINVAL;
+  if (any_too_big(m, n, k, lda, ldb, ldd, ld_as, sb_n, sb_k)) return PF8_ESHAPE;
   if (k % kGroup != 0) return PF8_ESHAPE;
   if (lda < k || ldb < k || ldd < n || ld_as < m || sb_n < 1 || sb_k < 1) return PF8_EINVAL;
   if (!aligned16(a) || !aligned16(b) || !aligned16(d) || !aligned4(a_dscale) || !aligned4(b_dscale)) return PF8_EALIGN;
@@ -162,6 +178,7 @@ pf8_status pf8_gemm_bf16(int64_t m, int64_t n, int64_t k, const void* a, int64_t
                   int64_t ldd, void* hip_stream) {
   if (a == nullptr || b == nullptr || d == nullptr) return PF8_EINVAL;
   if (m <= 0 || n <= 0 || k <= 0) return PF8_EINVAL;
+  if (any_too_big(m, n, k, lda, ldb, ldd)) return PF8_ESHAPE;
   if (k % kGroup != 0) return PF8_ESHAPE;
   if (lda < k || ldb < k || ldd < n) return PF8_EINVAL;
   if (!aligned16(a) || !aligned16(b) || !aligned16(d)) return PF8_EALIGN;

@@ -25,6 +25,8 @@
  *    exact powers of two 2^e, e in [-126, 120]; an all-zero block gets scale 1.
  *  - E4M3 is the OCP E4M3FN encoding (bias 7, max 448, no infinities), rounded to nearest-even,
  *    sign kept on zero. Inputs must be finite; NaN/Inf inputs give unspecified codes.
+ *  - Sizes: every dimension, leading dimension and scale stride is at most 2^31 - 1; a larger one
+ *    is refused with PF8_ESHAPE (no such array fits a GPU's memory).
  *  - Alignment: every code / bf16 array base is 16-byte aligned, and its row pitch
  *    (ld * element size) is a multiple of 16 bytes. Scale arrays are 4-byte aligned.
  *  - Row pitches and speed: a GEMM reads (and its epilogue writes) the same column slice of many
@@ -54,7 +56,7 @@ typedef int pf8_layout;
 /* Status codes (pf8_status). */
 #define PF8_OK 0
 #define PF8_EINVAL 1  /* null pointer, unknown enum value, non-positive dimension, ld too small */
-#define PF8_ESHAPE 2  /* a grouped / tiled dimension is not a multiple of 128 (or 8, see below) */
+#define PF8_ESHAPE 2  /* a grouped / tiled dimension is not a multiple of 128 (or 8, see below), or a size is too large */
 #define PF8_EALIGN 3  /* pointer not 16-byte aligned, or row pitch not a multiple of 16 bytes */
 #define PF8_ENODEV 4  /* no usable HIP device (the library loads and validates without one) */
 #define PF8_ELAUNCH 5 /* the kernel launch reported an error */
