@@ -294,7 +294,7 @@ __device__ __forceinline__ void interleave_groups() {
 // second 16 bytes hold K values {0..7, 16..23} and {8..15, 24..31} of the stage in both
 // operands, so every product of the stage is formed exactly once).
 template <int BM, int BN, bool ROW_B, bool EDGE, int NST, bool F32 = false, bool BF16IN = false>
-__global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, int tiles_n, int slots) {
   constexpr int BK = 64;
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   constexpr int A_ST = BM * BK, ST = (BM + BN) * BK;
@@ -320,6 +320,11 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
     const int nb = gridDim.x, xcd = bid & 7, q = nb >> 3, rem = nb & 7;
     bid = xcd * q + min(xcd, rem) + (bid >> 3);
   }
+  // Serpentine K: a tile of an odd round (its position in its XCD's sequence / slots, slots = the
+  // XCD's CUs) walks K from the end, starting on the K slices the previous round left in L2.
+  // The persistent kernel takes the same direction for the same tile, so the two sum every
+  // element in the same order. slots = 0: always forward.
+  const int rev = (!BF16IN && slots > 0) ? __builtin_amdgcn_readfirstlane(((blockIdx.x >> 3) / slots) & 1) : 0;
   constexpr int kGroupM = 8;
   const int per_group = kGroupM * tiles_n;
   const int grp = bid / per_group;
@@ -374,7 +379,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
     // with the direct-to-LDS loads around them. Every index therefore passes through an opaque
     // asm statement: the compiler can neither merge two loads whose addresses it proves equal
     // (known bits of clamped columns let it do so) nor hoist one above earlier loads.
-    const int64_t kb = s >> 1;
+    const int64_t kb = (rev ? ns - 1 - s : s) >> 1;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       int64_t idx = kb * p.ld_as + a_row[i];
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
     constexpr int u = decltype(u_c)::value;
     uint8_t* buf = bufs(u);
     if constexpr (!BF16IN && part != 0 && decltype(even_c)::value) load_scales(s, sc_a[u], sc_b[u]);
-    const int kofs = s * BK;
+    const int kofs = (rev ? ns - 1 - s : s) * BK;
 #pragma unroll
     for (int j = 0; j < (part == 1 ? 0 : A_DMA); ++j) {
       const int slab = wave + 4 * j;  // rows 16*slab .. +15 of the A tile
@@ -913,7 +918,9 @@ __global__ __launch_bounds__(256) void gemm_mx_persistent_kernel(GemmArgs p, int
   // ---- load state: the tile whose stages the refills fetch ----
   __amdgpu_buffer_rsrc_t rsrc_a, rsrc_b;
   int64_t a_row[TM], b_row[SB];
+  int load_rev = 0;  // odd tiles walk K from the end (serpentine, as gemm_mx_kernel's odd rounds)
   auto set_load_tile = [&](int r) {
+    load_rev = r & 1;
     int64_t m0, n0;
     tile_origin(r, m0, n0);
     rsrc_a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.a + m0 * p.lda), 0, BM * lda, kBufferFlags);
@@ -928,7 +935,7 @@ __global__ __launch_bounds__(256) void gemm_mx_persistent_kernel(GemmArgs p, int
   auto load_scales = [&](int s, uint32_t (&sa)[TM], uint32_t (&sb)[SB]) {
     // the waits count exactly TM + SB loads here: opaque indices keep the compiler from merging
     // two of them or hoisting one above earlier loads (as in gemm_mx_kernel)
-    const int64_t kb = s >> 1;
+    const int64_t kb = (load_rev ? ns - 1 - s : s) >> 1;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       int64_t idx = kb * p.ld_as + a_row[i];
@@ -949,7 +956,7 @@ __global__ __launch_bounds__(256) void gemm_mx_persistent_kernel(GemmArgs p, int
     constexpr int part = decltype(part_c)::value;
     uint8_t* buf = bufs(u);
     if constexpr (part == 1 && (u % 2 == 0)) load_scales(s, sc_a[u / 2], sc_b[u / 2]);
-    const int kofs = s * BK;
+    const int kofs = (load_rev ? ns - 1 - s : s) * BK;
 #pragma unroll
     for (int j = 0; j < (part == 0 ? A_DMA : 0); ++j) {
       const int slab = wave + 4 * j;
@@ -1191,6 +1198,7 @@ static hipError_t launch_tile(const GemmArgs& args, hipStream_t stream) {
   const int tiles_n = static_cast<int>((args.n + BN - 1) / BN);
   const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n)), block(256);
   const bool edge = args.m % BM != 0 || args.n % BN != 0;
+  const int slots = device_cus() / 8;  // one tile per CU and round
   if constexpr (MX) {
     // five stage buffers fit the 160 KB LDS for every tile shape here; K extents under five
     // stages take the two-buffer pipeline
@@ -1201,17 +1209,17 @@ static hipError_t launch_tile(const GemmArgs& args, hipStream_t stream) {
     constexpr bool kF32Tile = (BM == 256 && BN == 256) || (BM == 192 && BN == 256) || (BM == 128 && BN == 128);
     if (args.d32 != nullptr) {
       if constexpr (kF32Tile) {
-        if (ns >= 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 5, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
-        else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 2, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
+        if (ns >= 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 5, true>), grid, block, 0, stream, args, tiles_m, tiles_n, slots);
+        else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 2, true>), grid, block, 0, stream, args, tiles_m, tiles_n, slots);
       } else {
         return hipErrorInvalidValue;  // not reached: the FP32 tile choice offers only the shapes above
       }
     } else if (edge) {
-      if (ns >= 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 5>), grid, block, 0, stream, args, tiles_m, tiles_n);
-      else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 2>), grid, block, 0, stream, args, tiles_m, tiles_n);
+      if (ns >= 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 5>), grid, block, 0, stream, args, tiles_m, tiles_n, slots);
+      else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, true, 2>), grid, block, 0, stream, args, tiles_m, tiles_n, slots);
     } else {
-      if (ns >= 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, false, 5>), grid, block, 0, stream, args, tiles_m, tiles_n);
-      else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, false, 2>), grid, block, 0, stream, args, tiles_m, tiles_n);
+      if (ns >= 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, false, 5>), grid, block, 0, stream, args, tiles_m, tiles_n, slots);
+      else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, ROW_B, false, 2>), grid, block, 0, stream, args, tiles_m, tiles_n, slots);
     }
   } else {
     if (edge)
@@ -1235,14 +1243,15 @@ static hipError_t launch_bf16_tile(const GemmArgs& args, hipStream_t stream) {
   const int tiles_n = static_cast<int>((args.n + BN - 1) / BN);
   const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n)), block(256);
   const bool edge = args.m % BM != 0 || args.n % BN != 0;
+  const int slots = 0;  // the BF16 comparison GEMM walks K forward
   const int64_t ns = args.k / 64;
   if (ns < 2 || ns % 2 != 0) return hipErrorInvalidValue;  // the stage layout needs an even stage count
   if (edge) {
-    if (ns >= 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false, true, 5, false, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
-    else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false, true, 2, false, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
+    if (ns >= 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false, true, 5, false, true>), grid, block, 0, stream, args, tiles_m, tiles_n, slots);
+    else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false, true, 2, false, true>), grid, block, 0, stream, args, tiles_m, tiles_n, slots);
   } else {
-    if (ns >= 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false, false, 5, false, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
-    else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false, false, 2, false, true>), grid, block, 0, stream, args, tiles_m, tiles_n);
+    if (ns >= 5) hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false, false, 5, false, true>), grid, block, 0, stream, args, tiles_m, tiles_n, slots);
+    else hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false, false, 2, false, true>), grid, block, 0, stream, args, tiles_m, tiles_n, slots);
   }
   return hipGetLastError();
 }

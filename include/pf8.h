@@ -161,6 +161,12 @@ pf8_status pf8_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw,
  * the library is tested to on such data. With outliers in both operands an outlier product can
  * take the low bits of the other seven products of its group, and only the contract holds.
  *
+ * Order and repeatability. The FP32 sum of an element runs over K forward or backward, by the
+ * position of its output tile in the launch (tiles of odd rounds start at the end of K, where the
+ * previous round's reads are still cached). The same call on the same device gives the same bits
+ * every time; the same rows inside a GEMM of another shape may differ in the last bits of the
+ * FP32 sum, always within the contract. No atomics; no split of K across workgroups.
+ *
  * m, n >= 1 (any value), k % 128 == 0.
  * a: u8 [m, k] (pitch lda >= k), reduction dim contiguous.  a_dscale: f32, sa(kb, i) = a_dscale[kb * ld_as + i], ld_as >= m.
  * b: u8 [n, k] (pitch ldb >= k), reduction dim contiguous.  b_dscale: f32, with

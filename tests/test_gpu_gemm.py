@@ -713,17 +713,21 @@ def test_full_size_bf16_and_f32_gemms_sampled():
 
 
 # ---- persistent kernel: shapes with two tiles or more per CU, K a multiple of 256 ----
-# (M, N, K) per layout; each takes the persistent kernel: 256x256 tiles (four, two and a half, and
-# 2.1 per CU with a tile count that is not a multiple of 8) and 192x256 tiles.
-PERSISTENT = [("fprop", 4096, 16384, 512), ("dgrad", 5120, 8192, 768), ("fprop", 5120, 6912, 512),
-              ("wgrad", 12288, 2048, 1024), ("wgrad", 8192, 4096, 1024), ("fprop", 6144, 12288, 1024)]
+# (M, N, K) per layout. The tile-shape model picks the same shape for the BF16 and the FP32 result
+# on each of them, and the BF16 result takes the persistent kernel: 256x256 tiles (four, two, and
+# 3.97 rounds of one tile per CU, the last with a tile count that is not a multiple of 8) and
+# 192x256 tiles, with tile-scaled (fprop, dgrad) and row-scaled (wgrad) B operands.
+PERSISTENT = [("fprop", 4096, 16384, 512), ("dgrad", 8192, 4096, 768), ("fprop", 7936, 8448, 1024),
+              ("fprop", 4608, 8192, 1024), ("dgrad", 9216, 4096, 768),
+              ("wgrad", 12288, 2048, 1024), ("wgrad", 8192, 4096, 1024)]
 
 
 @pytest.mark.parametrize("lname,m,n,k", PERSISTENT, ids=lambda v: str(v))
 def test_persistent_kernel_matches_one_tile_kernel_and_oracle(lname, m, n, k):
-    """The persistent kernel sums every element's products in the one-tile kernel's order: its BF16
-    result equals the rounded result of the FP32 kernel (one tile per workgroup, same tile shape)
-    bit for bit; sampled rows, the first and last included, meet the oracle's bar."""
+    """The persistent kernel sums every element's products in the one-tile kernel's order (K
+    backward in the same odd rounds): its BF16 result equals the rounded result of the FP32 kernel
+    (one tile per workgroup, same tile shape) bit for bit; sampled rows, the first and last
+    included, meet the oracle's bar."""
     layout = LAYOUTS[lname]
     qa, sa, qb, sb, sb_n, sb_k, _ = _operands_nosample(layout, m, n, k, m + n + k)
     a, sa_d, b, sb_d = to_dev_u8(qa), to_dev_f32(sa), to_dev_u8(qb), to_dev_f32(sb)
