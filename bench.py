@@ -494,6 +494,10 @@ def main():
                    "launches_per_step": len(names), "title": wl.title},
         "pct_of_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
         "wall_ms_per_step": round(ms_step_wall, 4),
+        # every timed step and its fprop GEMM, in order: after an idle host phase the first few dozen
+        # steps run through the chip's power-management transient (clocks fall, then recover)
+        "step_us_each": [round(e[0].elapsed_time(e[-1]) * 1e3, 1) for e in evs],
+        "fprop_us_each": [round(v, 1) for v in per_all["fprop_gemm"]],
         "roofline": roofline,
         "kernels": kernels,
         "wgrad_f32_accumulate": {"us": round(f32_us, 2), "tflops": round(2.0 * m * n * k / (f32_us * 1e-6) / 1e12, 1),
