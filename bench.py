@@ -104,7 +104,32 @@ def run_step_timed(step, steps, torch):
     return [name for name, _ in launches], evs
 
 
-def time_comparators(torch, pf8, m, n, k, reps=20):
+def time_steady(torch, fn, reps=50, warm_ms=60.0):
+    """Per-launch times (us) of fn once the chip has settled: fn runs back to back for at least
+    warm_ms of GPU time first (after an idle host phase the clocks dip for some tens of ms), then
+    `reps` launches are timed one by one with events. Returns median, p10 and p90."""
+    st = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    start.record(st)
+    for _ in range(200):
+        for _ in range(10):
+            fn()
+        end = torch.cuda.Event(enable_timing=True)
+        end.record(st)
+        end.synchronize()
+        if start.elapsed_time(end) >= warm_ms:
+            break
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record(st)
+        fn()
+        e1.record(st)
+    torch.cuda.synchronize()
+    us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+    return float(np.median(us)), float(np.percentile(us, 10)), float(np.percentile(us, 90))
+
+
+def time_comparators(torch, pf8, m, n, k, reps=50):
     """On the fprop shape, as context: this library's plain BF16 GEMM (same pipeline, BF16
     operands), and hipBLASLt through torch: FP8 E4M3 with one scale per tensor and per row /
     column (not block scales), and BF16."""
@@ -124,24 +149,17 @@ def time_comparators(torch, pf8, m, n, k, reps=20):
         "hipblaslt_bf16": lambda: torch.mm(ab, bb.t()),
     }
     out = {}
-    st = torch.cuda.current_stream()
     for name, fn in cases.items():
         try:
-            for _ in range(3):
-                fn()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(st)
-            for _ in range(reps):
-                fn()
-            e1.record(st)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
-            out[name] = {"us": round(us, 2), "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)}
+            us, p10, p90 = time_steady(torch, fn, reps)
+            out[name] = {"us": round(us, 2), "us_p10": round(p10, 2), "us_p90": round(p90, 2),
+                         "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)}
         except Exception as ex:  # a comparator that torch cannot run is reported, not fatal
             out[name] = {"error": repr(ex)[:200]}
     del a, b, ab, bb, y16
     torch.cuda.empty_cache()
-    return {"shape": [m, n, k], "note": "library GEMMs without block scales; context only", **out}
+    return {"shape": [m, n, k], "note": "library GEMMs without block scales; context only; per-launch median, p10 "
+                                        "and p90 after at least 60 ms of back-to-back launches", **out}
 
 
 def device_peak_fp8():
@@ -198,8 +216,10 @@ def time_cold_warm(torch, fn, reps=20, flush_bytes=512 << 20):
     return out
 
 
-def time_config_gemms(pf8, torch, reps=20):
-    """Average kernel time of each configured GEMM (inputs quantised on the GPU first)."""
+def time_config_gemms(pf8, torch, reps=50):
+    """Kernel time of each configured GEMM (inputs quantised on the GPU first): per-launch median,
+    p10 and p90 of `reps` launches after at least 60 ms of back-to-back launches (the inputs are
+    built on the host, so the GPU comes out of an idle phase before every configuration)."""
     from workloads import WORKLOADS, generate
 
     out = {}
@@ -221,18 +241,10 @@ def time_config_gemms(pf8, torch, reps=20):
                 qxt, sxt = pf8.quant_act_1x128(dev["X"], "rows")
                 fn = lambda a=qdyt, sa=sdyt, b=qxt, sb=sxt: pf8.wgrad(a, sa, b, sb, out=y)  # noqa: E731
             y = pf8.ops.result_buffer(m, n, torch.bfloat16, "cuda:0")
-            for _ in range(3):
-                fn()
-            st = torch.cuda.current_stream()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(st)
-            for _ in range(reps):
-                fn()
-            e1.record(st)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
+            us, p10, p90 = time_steady(torch, fn, reps)
             tf = 2.0 * m * n * k / (us * 1e-6) / 1e12
-            out[f"{key}:{layout}"] = {"m": m, "n": n, "k": k, "us": round(us, 2), "tflops": round(tf, 1),
+            out[f"{key}:{layout}"] = {"m": m, "n": n, "k": k, "us": round(us, 2), "us_p10": round(p10, 2),
+                                      "us_p90": round(p90, 2), "tflops": round(tf, 1),
                                       "frac_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
         del dev
         torch.cuda.empty_cache()
