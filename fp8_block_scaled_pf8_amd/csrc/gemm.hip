@@ -1076,6 +1076,15 @@ __global__ __launch_bounds__(256) void gemm_mx_persistent_kernel(GemmArgs p, int
   issue_part(I3{}, 3, PA{});
   issue_part(I3{}, 3, PB{});
   __builtin_amdgcn_sched_barrier(0);
+  // Staggered start: with four tiles or more per workgroup, the odd slots of every XCD begin their
+  // first MFMAs about a third of a tile (half a tile's MFMA cycles) after the even ones, once
+  // their first stages are on the way. Every tile ends with a 128 KB burst of stores that the
+  // next tile's fourth stage waits behind (loads and stores complete in order); with all CUs in
+  // step those bursts coincide and take the HBM write rate for several microseconds. Offset, each
+  // half of the CUs stores while the other half computes.
+  if (ntiles >= 4 && (slot & 1)) {
+    for (int z = 0; z < ns; ++z) __builtin_amdgcn_s_sleep(TM * TN / 2);  // 64 * TM * TN / 2 cycles per stage
+  }
   PF8_WAIT_VM_LGKM0(D + (D + SS) + D);  // after stage 0: stages 1, 2 and 3
   __builtin_amdgcn_s_barrier();
   read_frags(buf0, fa[0], fb[0]);
