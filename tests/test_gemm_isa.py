@@ -173,7 +173,8 @@ def test_persistent_kernel_load_counts(asm):
         assert lds == 20 * a_dma + 19 * b_dma, f"{name}: {lds} direct-to-LDS loads"
         assert scale == 10 * ss, f"{name}: {scale} scale loads"
         assert stores == 8 * tm, f"{name}: {stores} stores"
-        loops = _inner_loops(body)
+        # the K loops (the staggered start's sleep loop holds no MFMA)
+        loops = [lp for lp in _inner_loops(body) if any(ln.strip().startswith("v_mfma") for ln in lp)]
         assert loops, name
         for lp in loops:
             n_lds = sum(1 for ln in lp if ln.strip().startswith("buffer_load_dword") and " lds" in ln)
