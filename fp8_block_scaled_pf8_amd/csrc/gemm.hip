@@ -1078,10 +1078,10 @@ __global__ __launch_bounds__(256) void gemm_mx_persistent_kernel(GemmArgs p, int
   __builtin_amdgcn_sched_barrier(0);
   // Staggered start: with four tiles or more per workgroup, the odd slots of every XCD begin their
   // first MFMAs about a third of a tile (half a tile's MFMA cycles) after the even ones, once
-  // their first stages are on the way. Every tile ends with a 128 KB burst of stores that the
-  // next tile's fourth stage waits behind (loads and stores complete in order); with all CUs in
-  // step those bursts coincide and take the HBM write rate for several microseconds. Offset, each
-  // half of the CUs stores while the other half computes.
+  // their first stages are on the way. Every tile ends with a 128 KB burst of stores per CU; with
+  // all CUs in step those bursts coincide (32 MB per round) and slow the epilogues and the loads
+  // of the next tiles' first stages. Offset, each half of the CUs stores while the other half
+  // computes.
   if (ntiles >= 4 && (slot & 1)) {
     for (int z = 0; z < ns; ++z) __builtin_amdgcn_s_sleep(TM * TN / 2);  // 64 * TM * TN / 2 cycles per stage
   }
