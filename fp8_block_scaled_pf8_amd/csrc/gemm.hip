@@ -33,6 +33,7 @@ namespace pf8 {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -765,6 +766,26 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs p, int tiles_m, i
   }
   __syncthreads();
   constexpr int PER_T = BM * CH / 256;  // chunks per thread
+  if constexpr (!EDGE && (CH & (CH - 1)) == 0) {
+    // whole tiles with power-of-two rows: buffer stores over the tile's rows, the lane's offset
+    // fixed and the chunk's row offset uniform (no 64-bit address arithmetic per store)
+    if (static_cast<int64_t>(BM) * p.ldd * 2 <= 0x7FFFFFFF) {
+      const __amdgpu_buffer_rsrc_t rsrc_d = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<uint8_t*>(p.d + m0 * p.ldd + n0), 0, static_cast<int>(BM * p.ldd * 2), kBufferFlags);
+      const int ldd2 = static_cast<int>(p.ldd * 2);
+      const int vo = (t / CH) * ldd2 + 16 * (t % CH);
+#pragma unroll
+      for (int it = 0; it < PER_T; ++it) {
+        const int q = t + 256 * it;
+        const int row = q / CH, c = q % CH;
+        const uint4 v = *reinterpret_cast<const uint4*>(bufs(static_cast<unsigned>(row) / RPB) +
+                                                        (static_cast<unsigned>(row) % RPB) * RP + phys(row, c) * 16);
+        const v4u nv = {v.x, v.y, v.z, v.w};
+        __builtin_amdgcn_raw_buffer_store_b128(nv, rsrc_d, vo, (256 / CH) * it * ldd2, 2);  // 2: non-temporal
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int it = 0; it < PER_T; ++it) {
     const int q = t + 256 * it;
@@ -866,7 +887,8 @@ __global__ __launch_bounds__(256) void gemm_mx_persistent_kernel(GemmArgs p, int
   __shared__ __align__(16) uint8_t buf1[ST];
   __shared__ __align__(16) uint8_t buf2[ST];
   __shared__ __align__(16) uint8_t buf3[ST];
-  __shared__ __align__(16) uint8_t stg[64 * RP];
+  // 512-byte aligned: a staged row's chunk offsets (bits 4..8) can be XORed into its base address
+  __shared__ __align__(512) uint8_t stg[64 * RP];
 
   const int t0 = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t0 >> 6);
@@ -1114,40 +1136,41 @@ __global__ __launch_bounds__(256) void gemm_mx_persistent_kernel(GemmArgs p, int
     // sr = wm*32 + lane%32; chunk c of staged row sr sits at chunk c ^ (sr mod 32) ----
     int64_t m0, n0;
     tile_origin(r, m0, n0);
-    auto phys = [](int row, int c) -> int { return c ^ (row & (CH - 1)); };
     constexpr int kWaitLgkm = 0xF | (0x7 << 4) | (0x3 << 14);  // lgkmcnt(0) only
+    // staging writes: this lane's row sr = wm*32 + l32 of the slab and its chunks c = wn*16 + k
+    // (k = 4j + q4), chunk c at c ^ l32: with a 512-byte aligned row the address is one XOR of k
+    const uint32_t wbase = (lds_addr(stg) + (wm * 32 + l32) * RP + 8 * half) | (((wn * 16) ^ l32) << 4);
+    // staging reads: thread t takes chunk t % 32 of rows t / 32 + 8 it, which sits at chunk slot
+    // (t % 32) ^ (t / 32) ^ 8 (it % 4)
+    const uint32_t rbase = (lds_addr(stg) + (t >> 5) * RP) | (((t & 31) ^ (t >> 5)) << 4);
+    // stores: a buffer resource over the tile's rows; the lane's offset is fixed per tile, the
+    // slab's and the chunk's row offsets are uniform
+    const __amdgpu_buffer_rsrc_t rsrc_d = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<uint8_t*>(p.d + m0 * p.ldd + n0), 0, static_cast<int>(BM * p.ldd * 2), kBufferFlags);
+    const int ldd2 = static_cast<int>(p.ldd * 2);
+    const int vo = (t >> 5) * ldd2 + 16 * (t & 31);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      {
-        const int sr = wm * 32 + l32;
-        const uint32_t rb = lds_addr(stg) + sr * RP;
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int c = (wn * WN + 32 * j + 8 * q4) >> 3;
-            const uint32_t w0 = pack_bf16x2(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1]);
-            const uint32_t w1 = pack_bf16x2(acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]);
-            stg_write8(rb + phys(sr, c) * 16 + 8 * half, w0, w1);
-          }
-      }
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const uint32_t w0 = pack_bf16x2(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1]);
+          const uint32_t w1 = pack_bf16x2(acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]);
+          stg_write8(wbase ^ ((4 * j + q4) << 4), w0, w1);
+        }
       __builtin_amdgcn_s_waitcnt(kWaitLgkm);
       __builtin_amdgcn_s_barrier();
       uint32_t ra[ST_STORES];
       v4i rv[ST_STORES];
 #pragma unroll
-      for (int it = 0; it < ST_STORES; ++it) {
-        const int qq = t + 256 * it;
-        const int row = qq / CH, c = qq % CH;
-        ra[it] = lds_addr(stg) + row * RP + phys(row, c) * 16;
-      }
+      for (int it = 0; it < ST_STORES; ++it) ra[it] = (rbase + 8 * it * RP) ^ ((it & 3) << 7);
       stg_read8x16(ra, rv);
 #pragma unroll
       for (int it = 0; it < ST_STORES; ++it) {
-        const int qq = t + 256 * it;
-        const int row = qq / CH, c = qq % CH;
-        const int64_t gm = m0 + (row >> 5) * WM + 32 * i + (row & 31), gn = n0 + 8 * c;
-        __builtin_nontemporal_store(rv[it], reinterpret_cast<v4i*>(p.d + gm * p.ldd + gn));
+        // row (it / 4) * WM + 32 i + 8 (it % 4) + t / 32 of the tile
+        const int so = ((it >> 2) * WM + 32 * i + 8 * (it & 3)) * ldd2;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, rv[it]), rsrc_d, vo, so, 2);
       }
       if (i + 1 < TM) {
         // every wave has read this slab back before the next one is staged
@@ -1193,6 +1216,7 @@ static hipError_t launch_persistent(const GemmArgs& args, bool row_b, hipStream_
   const int64_t tiles_m = args.m / BM, tiles_n = args.n / 256;
   const int grid = device_cus() / 8 * 8;
   if (grid < 8 || tiles_m * tiles_n < 2 * static_cast<int64_t>(grid)) return hipErrorNotSupported;
+  if (static_cast<int64_t>(BM) * args.ldd * 2 > 0x7FFFFFFF) return hipErrorNotSupported;  // a tile's rows in one buffer range
   const int tm = static_cast<int>(tiles_m), tn = static_cast<int>(tiles_n);
   if (row_b)
     hipLaunchKernelGGL((gemm_mx_persistent_kernel<BM, true>), dim3(grid), dim3(256), 0, stream, args, tm, tn);

@@ -169,7 +169,7 @@ def test_persistent_kernel_load_counts(asm):
         ss = tm + (4 if row_b else 1)
         lds = sum(1 for ln in body if ln.strip().startswith("buffer_load_dword") and " lds" in ln)
         scale = sum(1 for ln in body if ln.strip().startswith("global_load_dword "))
-        stores = sum(1 for ln in body if ln.strip().startswith("global_store"))
+        stores = sum(1 for ln in body if ln.strip().startswith(("global_store", "buffer_store")))
         assert lds == 20 * a_dma + 19 * b_dma, f"{name}: {lds} direct-to-LDS loads"
         assert scale == 10 * ss, f"{name}: {scale} scale loads"
         assert stores == 8 * tm, f"{name}: {stores} stores"
@@ -179,7 +179,7 @@ def test_persistent_kernel_load_counts(asm):
         for lp in loops:
             n_lds = sum(1 for ln in lp if ln.strip().startswith("buffer_load_dword") and " lds" in ln)
             n_sc = sum(1 for ln in lp if ln.strip().startswith("global_load_dword "))
-            n_st = sum(1 for ln in lp if ln.strip().startswith("global_store"))
+            n_st = sum(1 for ln in lp if ln.strip().startswith(("global_store", "buffer_store")))
             assert (n_lds, n_sc, n_st) == (4 * (a_dma + b_dma), 2 * ss, 0), f"{name}: loop trip {n_lds}, {n_sc}, {n_st}"
         checked += 1
     assert checked == 4, checked
