@@ -14,7 +14,10 @@
 //    rows; an FP32 form writes (or adds to) an FP32 result. Details above the kernel.
 //  * gemm_mx_persistent_kernel: the same tiles and arithmetic, one workgroup per CU walking its
 //    tiles with a ring of stage buffers that runs across tile boundaries (taken when every CU
-//    gets two tiles or more, BF16 results, K a multiple of 256).
+//    gets two tiles or more, BF16 results, K a multiple of 256); with four tiles or more, half of
+//    the workgroups start late so that the CUs' output bursts do not coincide.
+//  * In both MX kernels the tiles of odd rounds walk K from its end (serpentine K), starting on
+//    the K slices the previous round left in L2; a tile takes the same direction in either.
 //  * gemm_promote_kernel: register-staged, double-buffered LDS; one v_mfma_f32_16x16x128_f8f6f4
 //    covers a whole 128-wide scale block with a zero accumulator, and its FP32 partial is folded
 //    into the running accumulator with one FMA by sa*sb per element.
