@@ -4,6 +4,8 @@
   (8,388,480 bytes of codes per row). Small ragged M and N put it on one edge tile, and all
   65,535 K blocks carry their own scales. Compared element by element with the oracle, for
   FP32 and BF16 results.
+- GEMM output rows so far apart that a 256-row tile spans more than 2 GB: the kernels' buffer
+  stores do not apply and plain 64-bit addresses take over.
 - Quantisers: 65,535 grid rows of 128-groups, i.e. the largest grouped dimension each kernel
   accepts. The row-mode case is compared in full. The 2 GB cases are compared on sampled
   128-row bands, always including the first and the last; bands quantise independently.
@@ -17,7 +19,7 @@ import torch
 import fp8_block_scaled_pf8_amd as pf8
 import oracle
 from workloads import f32_to_bf16_bits
-from tests.gpu_helpers import DEV, bf16_bits, f32, to_dev_bf16, to_dev_f32, to_dev_u8, u8
+from tests.gpu_helpers import DEV, bf16_bits, bf16_f64, f32, to_dev_bf16, to_dev_f32, to_dev_u8, u8
 
 pytestmark = pytest.mark.gpu
 
@@ -168,3 +170,30 @@ def test_gemm_beyond_2g_operand_elements():
     got64 = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     rep = oracle.gemm_tolerance_report(got64, ref)
     assert rep["violations"] == 0, rep
+
+
+def test_gemm_output_pitch_beyond_buffer_range():
+    """A BF16 result whose 256-row tiles span more than 2 GB (row pitch 4,194,432 elements): the
+    stores cannot use one buffer range per tile, and both kernels that would (the persistent one,
+    which this shape's 512 tiles would take, and the one-tile kernel) fall back to plain 64-bit
+    addresses. Sampled rows against the oracle; the padding after each sampled row untouched."""
+    m, n, k = 512, 65536, 512
+    ldd = (1 << 22) + 128  # 256 * ldd * 2 bytes > 2^31 - 1
+    rng = np.random.default_rng(41)
+    qa, qb = _codes(rng, (m, k)), _codes(rng, (n, k))
+    sa = _pow2(rng, (k // G, m))
+    sb = _pow2(rng, (n // G, k // G))  # W's tile grid
+    a, b, sa_d, sb_d = to_dev_u8(qa), to_dev_u8(qb), to_dev_f32(sa), to_dev_f32(sb)
+    buf = torch.full((m, ldd), -7.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[:, :n]
+    pf8.block_gemm(pf8.PF8_FPROP, a, sa_d, b, sb_d, sb.shape[1], 1, out=out)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 300, m - 1])
+    got = bf16_f64(out[torch.from_numpy(rows).to(DEV)])
+    ref = oracle.gemm_fprop(qa[rows], sa[:, rows], qb, sb)
+    rep = oracle.gemm_tolerance_report(got, ref)
+    assert rep["violations"] == 0, rep
+    pad = buf[torch.from_numpy(rows).to(DEV), n:n + 4096].float().cpu().numpy()
+    assert np.all(pad == -7.0)
+    del buf, out
+    torch.cuda.empty_cache()
