@@ -57,7 +57,8 @@ def parse_args():
                          "dY quantiser, or only a 1 GiB device copy (the calibration kernel for the FETCH_SIZE / "
                          "WRITE_SIZE counters), --steps times")
     ap.add_argument("--summarize-prof", nargs="+", metavar="DIR", default=None,
-                    help="print a text summary of rocprofv3 csv output directories and exit")
+                    help="print a text summary of rocprofv3 csv output directories and exit (with --steps: "
+                         "the number of timed steps at the end of a traced run of layer steps)")
     return ap.parse_args()
 
 
@@ -129,23 +130,30 @@ def settle(torch, fn, warm_ms):
     return runs, ms
 
 
-def time_steady(torch, fn, reps=50, warm_ms=SETTLE_MS):
+def time_steady(torch, fn, reps=50, warm_ms=SETTLE_MS, group=10):
     """Per-launch times (us) of fn once the chip has settled: fn runs back to back for at least
     warm_ms of GPU time first (after an idle host phase the clocks dip for some tens of ms), then
-    `reps` launches are timed one by one with events. Returns median, p10 and p90."""
+    `reps` launches run in groups of `group` back-to-back launches with an event between groups
+    (an event between every two launches would add its marker's gap, some microseconds, to each).
+    Returns the median, p10 and p90 over the groups of their mean time per launch, and the host's
+    time per launch to enqueue them (a GPU time close to it would be the host's launch rate)."""
     st = torch.cuda.current_stream()
     settle(torch, fn, warm_ms)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for e0, e1 in evs:
-        e0.record(st)
-        fn()
-        e1.record(st)
+    ngroups = max(reps // group, 1)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(ngroups + 1)]
+    t0 = time.perf_counter()
+    evs[0].record(st)
+    for g in range(ngroups):
+        for _ in range(group):
+            fn()
+        evs[g + 1].record(st)
+    host_us = (time.perf_counter() - t0) * 1e6 / (ngroups * group)
     torch.cuda.synchronize()
-    us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
-    return float(np.median(us)), float(np.percentile(us, 10)), float(np.percentile(us, 90))
+    us = np.array([evs[g].elapsed_time(evs[g + 1]) * 1e3 / group for g in range(ngroups)])
+    return float(np.median(us)), float(np.percentile(us, 10)), float(np.percentile(us, 90)), host_us
 
 
-def time_comparators(torch, pf8, m, n, k, reps=50):
+def time_comparators(torch, pf8, m, n, k, reps=100):
     """On the fprop shape, as context: this library's plain BF16 GEMM (same pipeline, BF16
     operands), and hipBLASLt through torch: FP8 E4M3 with one scale per tensor and per row /
     column (not block scales), and BF16."""
@@ -167,8 +175,9 @@ def time_comparators(torch, pf8, m, n, k, reps=50):
     out = {}
     for name, fn in cases.items():
         try:
-            us, p10, p90 = time_steady(torch, fn, reps)
+            us, p10, p90, host_us = time_steady(torch, fn, reps)
             out[name] = {"us": round(us, 2), "us_p10": round(p10, 2), "us_p90": round(p90, 2),
+                         "host_us_per_launch": round(host_us, 1),
                          "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)}
         except Exception as ex:  # a comparator that torch cannot run is reported, not fatal
             out[name] = {"error": repr(ex)[:200]}
@@ -232,10 +241,11 @@ def time_cold_warm(torch, fn, reps=20, flush_bytes=512 << 20):
     return out
 
 
-def time_config_gemms(pf8, torch, reps=50):
-    """Kernel time of each configured GEMM (inputs quantised on the GPU first): per-launch median,
-    p10 and p90 of `reps` launches after at least 60 ms of back-to-back launches (the inputs are
-    built on the host, so the GPU comes out of an idle phase before every configuration)."""
+def time_config_gemms(pf8, torch, reps=100):
+    """Kernel time of each configured GEMM (inputs quantised on the GPU first): median, p10 and p90
+    over groups of 10 back-to-back launches of the mean time per launch, `reps` launches in all,
+    after at least 60 ms of back-to-back launches (the inputs are built on the host, so the GPU
+    comes out of an idle phase before every configuration)."""
     from workloads import WORKLOADS, generate
 
     out = {}
@@ -257,10 +267,11 @@ def time_config_gemms(pf8, torch, reps=50):
                 qxt, sxt = pf8.quant_act_1x128(dev["X"], "rows")
                 fn = lambda a=qdyt, sa=sdyt, b=qxt, sb=sxt: pf8.wgrad(a, sa, b, sb, out=y)  # noqa: E731
             y = pf8.ops.result_buffer(m, n, torch.bfloat16, "cuda:0")
-            us, p10, p90 = time_steady(torch, fn, reps)
+            us, p10, p90, host_us = time_steady(torch, fn, reps)
             tf = 2.0 * m * n * k / (us * 1e-6) / 1e12
             out[f"{key}:{layout}"] = {"m": m, "n": n, "k": k, "us": round(us, 2), "us_p10": round(p10, 2),
-                                      "us_p90": round(p90, 2), "tflops": round(tf, 1),
+                                      "us_p90": round(p90, 2), "host_us_per_launch": round(host_us, 1),
+                                      "tflops": round(tf, 1),
                                       "frac_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
         del dev
         torch.cuda.empty_cache()
@@ -370,8 +381,11 @@ def only_mode(args, torch, pf8):
                       "launches": args.steps, "gemm_source_sha256_16": gemm_source_hash()}), flush=True)
 
 
-def summarize_prof(dirs):
-    """Text summary of rocprofv3 csv directories: kernel stats and per-dispatch counter averages."""
+def summarize_prof(dirs, timed_steps=50):
+    """Text summary of rocprofv3 csv directories: kernel stats and per-dispatch counter averages.
+    For a kernel trace of the layer step, also the per-launch-position averages over every step
+    after the first two, over the timed steps and over the event-timed steps that follow them
+    (`timed_steps` each, at the end of the run of steps), with the mean gap between launches."""
     import csv
     import glob
     from collections import defaultdict
@@ -395,12 +409,24 @@ def summarize_prof(dirs):
             while (nsteps + 1) * len(kernels) <= len(names) and \
                     names[nsteps * len(kernels):(nsteps + 1) * len(kernels)] == names[:len(kernels)]:
                 nsteps += 1
-            if nsteps >= 3:
-                skip = 2  # warm-up steps
+            nk = len(kernels)
+
+            def positions(label, lo, hi):
                 for j, name in enumerate(kernels):
-                    v = [seq[i * len(kernels) + j] for i in range(skip, nsteps)]
-                    print(f"step position {name}: dispatches={len(v)} avg_ns={sum(v) / len(v):.0f} "
+                    v = [seq[i * nk + j] for i in range(lo, hi)]
+                    print(f"{label} {name}: dispatches={len(v)} avg_ns={sum(v) / len(v):.0f} "
                           f"min_ns={min(v)} max_ns={max(v)}")
+                gaps = [int(pf8_rows[i * nk + j + 1]["Start_Timestamp"]) - int(pf8_rows[i * nk + j]["End_Timestamp"])
+                        for i in range(lo, hi) for j in range(nk - 1)]
+                print(f"{label} gap between launches: avg_ns={sum(gaps) / len(gaps):.0f}")
+
+            if nsteps >= 3:
+                positions("step position", 2, nsteps)  # every step but the first two
+            if nsteps >= 2 * timed_steps:
+                # bench.py ends its run of steps with the timed steps (no event between launches),
+                # then as many steps with an event after every launch (the per-launch breakdown)
+                positions("timed step position", nsteps - 2 * timed_steps, nsteps - timed_steps)
+                positions("event-timed step position", nsteps - timed_steps, nsteps)
         for f in sorted(glob.glob(os.path.join(d, "*counter_collection.csv"))):
             agg = defaultdict(list)
             for r in csv.DictReader(open(f)):
@@ -412,7 +438,7 @@ def summarize_prof(dirs):
 def main():
     args = parse_args()
     if args.summarize_prof:
-        summarize_prof(args.summarize_prof)
+        summarize_prof(args.summarize_prof, args.steps)
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); the path has no multi-GPU "
@@ -447,13 +473,24 @@ def main():
     settle_steps, settle_ms = settle(torch, step.run, SETTLE_MS)
     for _ in range(args.warmup):
         step.run()
+    st = torch.cuda.current_stream()
+    # The timed steps: exactly --steps steps with one event before and one after them, as a
+    # training loop runs them (no event between launches).
+    ev_start, ev_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    names, evs = run_step_timed(step, args.steps, torch)
+    ev_start.record(st)
+    for _ in range(args.steps):
+        step.run()
+    ev_end.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step_wall = wall * 1e3 / args.steps
-    # per-kernel averages from the events (same stream as the launches)
+    ms_step = ev_start.elapsed_time(ev_end) / args.steps
+    # The per-launch breakdown: as many steps again, with an event after every launch (on the
+    # launch stream). Each event costs the step a few microseconds, so these steps run longer.
+    names, evs = run_step_timed(step, args.steps, torch)
+    torch.cuda.synchronize()
     per = {name: 0.0 for name in names}
     per_all = {name: [] for name in names}
     gpu_ms = 0.0
@@ -464,7 +501,7 @@ def main():
             per_all[name].append(dt * 1e3)
         gpu_ms += e[0].elapsed_time(e[-1])
     per = {kname: v / args.steps for kname, v in per.items()}
-    ms_step = gpu_ms / args.steps
+    ms_step_instr = gpu_ms / args.steps
     flops = step.flops()
     value = flops / (ms_step * 1e-3) / 1e12
     kernels = {}
@@ -483,9 +520,8 @@ def main():
     # the FP32 weight gradient accumulated into a main gradient (pf8_block_gemm_f32, accumulate=1), on
     # the step's own codes, timed the same way: reported beside the step, not part of it
     main_grad = torch.zeros((n, k), dtype=torch.float32, device="cuda:0")
-    st = torch.cuda.current_stream()
-    for _ in range(3):
-        pf8.wgrad_f32(step.qdyt, step.sdyt, step.qxt, step.sxt, out=main_grad, accumulate=True)
+    settle(torch, lambda: pf8.wgrad_f32(step.qdyt, step.sdyt, step.qxt, step.sxt, out=main_grad, accumulate=True),
+           SETTLE_MS)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(st)
     for _ in range(20):
@@ -495,8 +531,7 @@ def main():
     f32_us = e0.elapsed_time(e1) * 1e3 / 20
     del main_grad
     # a later micro-batch of the same optimizer step: W's codes (made by the steps above) reused
-    for _ in range(3):
-        step.run(weight_codes=False)
+    settle(torch, lambda: step.run(weight_codes=False), SETTLE_MS)  # after a change of load, too, the clocks move
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(st)
     for _ in range(args.steps):
@@ -529,7 +564,9 @@ def main():
                    "launches_per_step": len(names), "title": wl.title},
         "pct_of_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
         "wall_ms_per_step": round(ms_step_wall, 4),
-        # every timed step and its fprop GEMM, in order (a step inside a clock transient shows here)
+        "instrumented_ms_per_step": round(ms_step_instr, 4),
+        # every step of the per-launch breakdown and its fprop GEMM, in order (a step inside a clock
+        # transient would show here)
         "step_us_each": [round(e[0].elapsed_time(e[-1]) * 1e3, 1) for e in evs],
         "fprop_us_each": [round(v, 1) for v in per_all["fprop_gemm"]],
         "roofline": roofline,

@@ -78,7 +78,9 @@ def test_device_peak_from_rocminfo(monkeypatch):
 
 
 def test_profile_summary_step_positions(tmp_path, capsys):
-    """The per-position view takes the leading run of whole steps and stops at other launches."""
+    """The per-position view takes the leading run of whole steps and stops at other launches. It
+    averages every step but the first two, then the timed steps and the event-timed steps that end
+    the run (timed_steps each), with the mean gap between a step's launches."""
     b = _bench()
     step = ["pf8::quant_fwd_kernel(pf8::FwdQuantArgs)",
             "void pf8::gemm_mx_kernel<256, 256, false, false, 5, false, false>(pf8::GemmArgs, int, int)",
@@ -86,11 +88,12 @@ def test_profile_summary_step_positions(tmp_path, capsys):
             "void pf8::gemm_mx_kernel<256, 256, false, false, 5, false, false>(pf8::GemmArgs, int, int)",
             "void pf8::gemm_mx_kernel<192, 256, true, false, 5, false, false>(pf8::GemmArgs, int, int)"]
     rows, t = [], 0
-    for i in range(4):  # 4 steps: 2 warm-up + 2 counted
+    for i in range(9):  # steps 0-2: settle and warm-up, 3-5: timed, 6-8: event-timed (wider gaps)
+        gap = 500 if i >= 6 else 10
         for j, name in enumerate(step):
             dur = 1000 * (j + 1) + i
             rows.append({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur})
-            t += dur + 10
+            t += dur + gap
     for _ in range(2):  # FP32-accumulate launches after the step, not part of it
         rows.append({"Kernel_Name": "void pf8::gemm_mx_kernel<192, 256, true, true, 5, true, false>(...)",
                      "Start_Timestamp": t, "End_Timestamp": t + 99999})
@@ -99,9 +102,12 @@ def test_profile_summary_step_positions(tmp_path, capsys):
         wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
         wr.writeheader()
         wr.writerows(rows)
-    b.summarize_prof([str(tmp_path)])
-    lines = [ln for ln in capsys.readouterr().out.splitlines() if ln.startswith("step position")]
-    assert [ln.split(":")[0].split()[-1] for ln in lines] == b.KERNELS_FUSED
-    for j, ln in enumerate(lines):
-        assert "dispatches=2" in ln
-        assert f"avg_ns={1000 * (j + 1) + 2.5:.0f}" in ln or f"avg_ns={1000 * (j + 1) + 2}" in ln
+    b.summarize_prof([str(tmp_path)], timed_steps=3)
+    out = capsys.readouterr().out.splitlines()
+    for label, steps, mean_i, gap in (("step position", 7, 5, (16 * 10 + 12 * 500) / 28),
+                                      ("timed step position", 3, 4, 10), ("event-timed step position", 3, 7, 500)):
+        lines = [ln for ln in out if ln.startswith(label + " ") and "gap between" not in ln]
+        assert [ln.split(":")[0].split()[-1] for ln in lines] == b.KERNELS_FUSED
+        for j, ln in enumerate(lines):
+            assert f"dispatches={steps} avg_ns={1000 * (j + 1) + mean_i} " in ln
+        assert f"{label} gap between launches: avg_ns={gap:.0f}" in out
