@@ -244,11 +244,13 @@ __device__ __forceinline__ int dual_slot(int c, int s) {
 
 // (red: [wave][column chunk][packed column pair] words of LDS, tile: kGroup * kGroup bytes of LDS;
 // gc = column group (row mode), gr = row group (col mode))
-// NT_IN: the BF16 input is read with non-temporal loads, so a tensor that is read once does not
-// displace what the following GEMMs read from the caches (the standalone dual quantiser on dY of
-// the gate+up layer step: step 652.0 -> 631.6 us, the weight gradient 191.7 -> 177.9 us; the
-// forward quantiser, whose codes fprop reads next, keeps cached loads).
-template <bool NT_IN>
+// The BF16 input is read with non-temporal loads, so a tensor that is read once does not displace
+// what the following GEMMs read from the caches. The standalone dual quantiser on dY of the
+// gate+up layer step: step 652.0 -> 631.6 us, the weight gradient 191.7 -> 177.9 us. The forward
+// quantiser's X tiles, interleaved A/B over 15 rounds: dgrad 3.1 us and wgrad 2.2 us faster, the
+// step 5.5 us (the likely reason: more of the weight codes and of X's transposed codes, which
+// those GEMMs read, stay in the caches). The weight tiles keep cached loads: non-temporal ones
+// there slowed fprop.
 __device__ __forceinline__ void quant_dual_tile(const uint16_t* __restrict__ x, int64_t ldx, uint8_t* __restrict__ qr,
                                                 int64_t ldqr, float* __restrict__ sr, int64_t ld_sr,
                                                 uint8_t* __restrict__ qc, int64_t ldqc, float* __restrict__ sc,
@@ -263,8 +265,7 @@ __device__ __forceinline__ void quant_dual_tile(const uint16_t* __restrict__ x, 
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const uint16_t* src = x + (r0 + 8 * rb + p) * ldx + c0 + 8 * cc;
-    if constexpr (NT_IN) v[p] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const pf8_u32x4*>(src)));
-    else v[p] = *reinterpret_cast<const uint4*>(src);
+    v[p] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const pf8_u32x4*>(src)));
   }
 
   // ---- row mode: 8 rows, one 128-value group each ----
@@ -351,7 +352,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
                                                          float* __restrict__ sc, int64_t ld_sc) {
   __shared__ __align__(16) uint32_t red[4][16][4];
   __shared__ __align__(16) uint8_t tile[kGroup * kGroup];
-  quant_dual_tile<true>(x, ldx, qr, ldqr, sr, ld_sr, qc, ldqc, sc, ld_sc, blockIdx.x, blockIdx.y, red, tile);
+  quant_dual_tile(x, ldx, qr, ldqr, sr, ld_sr, qc, ldqc, sc, ld_sc, blockIdx.x, blockIdx.y, red, tile);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(256) void quant_fwd_kernel(FwdQuantArgs a) {
                  &red[0][0][0], tile);
   } else {
     const int64_t bx = b - a.w_tiles;
-    quant_dual_tile<false>(a.x, a.ldx, a.qx, a.ldqx, a.sx, a.ld_sx, a.qxt, a.ldqxt, a.sxt, a.ld_sxt, bx % a.x_col_groups,
+    quant_dual_tile(a.x, a.ldx, a.qx, a.ldqx, a.sx, a.ld_sx, a.qxt, a.ldqxt, a.sxt, a.ld_sxt, bx % a.x_col_groups,
                     bx / a.x_col_groups, red, tile);
   }
 }
