@@ -381,6 +381,41 @@ def only_mode(args, torch, pf8):
                       "launches": args.steps, "gemm_source_sha256_16": gemm_source_hash()}), flush=True)
 
 
+def _counter_step_positions(path, timed_steps):
+    """Per launch position of the layer step, the counters of the timed steps (the run of whole
+    steps ends with the timed steps, then as many event-timed ones), and for the GEMMs the MFMA
+    busy cycles per SIMD (1024 SIMDs) over the GPU-active cycles per XCD (8 XCDs)."""
+    import csv
+    from collections import OrderedDict
+
+    disp = OrderedDict()
+    for r in csv.DictReader(open(path)):
+        rec = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+                                                      "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        rec[r["Counter_Name"]] = float(r["Counter_Value"])
+    pf8_rows = [disp[i] for i in sorted(disp) if "pf8::" in disp[i]["name"]]
+    names = [r["name"] for r in pf8_rows]
+    kernels = KERNELS_FUSED if any("quant_fwd" in n for n in names) else KERNELS_UNFUSED
+    nk = len(kernels)
+    nsteps = 0
+    while (nsteps + 1) * nk <= len(names) and names[nsteps * nk:(nsteps + 1) * nk] == names[:nk]:
+        nsteps += 1
+    if nsteps < 2 * timed_steps:
+        return
+    lo, hi = nsteps - 2 * timed_steps, nsteps - timed_steps
+    for j, kname in enumerate(kernels):
+        v = [pf8_rows[i * nk + j] for i in range(lo, hi)]
+        counters = sorted(c for c in v[0] if c not in ("name", "ns"))
+        avg = {c: sum(x[c] for x in v) / len(v) for c in counters}
+        ns = sum(x["ns"] for x in v) / len(v)
+        line = " ".join(f"{c}={avg[c]:.6g}" for c in counters)
+        print(f"timed step position {kname}: dispatches={len(v)} avg_ns={ns:.0f} {line}")
+        if avg.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) > 0 and avg.get("GRBM_GUI_ACTIVE", 0) > 0:
+            busy, act = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024, avg["GRBM_GUI_ACTIVE"] / 8
+            print(f"timed step position {kname}: mfma_busy_cycles_per_simd={busy:.0f} "
+                  f"active_cycles_per_xcd={act:.0f} mfma_busy_frac={busy / act:.3f}")
+
+
 def summarize_prof(dirs, timed_steps=50):
     """Text summary of rocprofv3 csv directories: kernel stats and per-dispatch counter averages.
     For a kernel trace of the layer step, also the per-launch-position averages over every step
@@ -433,6 +468,7 @@ def summarize_prof(dirs, timed_steps=50):
                 agg[(r["Kernel_Name"][:90], r["Counter_Name"])].append(float(r["Counter_Value"]))
             for (kname, cname), v in sorted(agg.items()):
                 print(f"counter {cname} kernel {kname}: dispatches={len(v)} avg={sum(v) / len(v):.6g}")
+            _counter_step_positions(f, timed_steps)
 
 
 def main():

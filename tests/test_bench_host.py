@@ -111,3 +111,43 @@ def test_profile_summary_step_positions(tmp_path, capsys):
         for j, ln in enumerate(lines):
             assert f"dispatches={steps} avg_ns={1000 * (j + 1) + mean_i} " in ln
         assert f"{label} gap between launches: avg_ns={gap:.0f}" in out
+
+
+def test_profile_summary_counter_step_positions(tmp_path, capsys):
+    """Counter view of the layer step: per launch position, the timed steps' counter averages (the
+    run of steps ends with timed_steps timed and as many event-timed steps), and for a GEMM the MFMA
+    busy cycles per SIMD over the active cycles per XCD."""
+    b = _bench()
+    step = ["pf8::quant_fwd_kernel(pf8::FwdQuantArgs)",
+            "void pf8::gemm_mx_persistent_kernel<256, false>(pf8::GemmArgs, int, int)",
+            "pf8::quant_dual_kernel(unsigned short const*)",
+            "void pf8::gemm_mx_kernel<256, 256, false, false, 5, false, false>(pf8::GemmArgs, int, int)",
+            "void pf8::gemm_mx_persistent_kernel<192, true>(pf8::GemmArgs, int, int)"]
+    rows, disp, t = [], 0, 0
+    for i in range(7):  # steps 0: warm-up, 1-3: timed, 4-6: event-timed
+        for j, name in enumerate(step):
+            disp += 1
+            active = 8000.0 * (j + 1) + (0 if 1 <= i <= 3 else 1e6)  # only the timed steps give the expected mean
+            busy = 1024.0 * 600 * (j % 2)  # the GEMM positions (1, 3) are busy 600 cycles per SIMD
+            for cname, val in (("GRBM_GUI_ACTIVE", active), ("SQ_VALU_MFMA_BUSY_CYCLES", busy)):
+                rows.append({"Dispatch_Id": disp, "Kernel_Name": name, "Counter_Name": cname, "Counter_Value": val,
+                             "Start_Timestamp": t, "End_Timestamp": t + 100 * (j + 1)})
+            t += 1000
+    rows.append({"Dispatch_Id": disp + 1, "Kernel_Name": "void pf8::gemm_mx_kernel<192, 256, true, true, 5, true, false>",
+                 "Counter_Name": "GRBM_GUI_ACTIVE", "Counter_Value": 1.0, "Start_Timestamp": t, "End_Timestamp": t + 1})
+    path = tmp_path / "pmc_counter_collection.csv"
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                                           "Start_Timestamp", "End_Timestamp"])
+        wr.writeheader()
+        wr.writerows(rows)
+    b._counter_step_positions(str(path), 3)
+    out = capsys.readouterr().out.splitlines()
+    for j, name in enumerate(b.KERNELS_FUSED):
+        assert f"timed step position {name}: dispatches=3 avg_ns={100 * (j + 1)} GRBM_GUI_ACTIVE={8000 * (j + 1)} " in \
+            next(ln for ln in out if ln.startswith(f"timed step position {name}: dispatches"))
+    busy = [ln for ln in out if "mfma_busy_frac" in ln]
+    assert busy == ["timed step position fprop_gemm: mfma_busy_cycles_per_simd=600 active_cycles_per_xcd=2000 "
+                    "mfma_busy_frac=0.300",
+                    "timed step position dgrad_gemm: mfma_busy_cycles_per_simd=600 active_cycles_per_xcd=4000 "
+                    "mfma_busy_frac=0.150"]
