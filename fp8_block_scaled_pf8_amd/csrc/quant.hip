@@ -352,7 +352,11 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
                                                          float* __restrict__ sc, int64_t ld_sc) {
   __shared__ __align__(16) uint32_t red[4][16][4];
   __shared__ __align__(16) uint8_t tile[kGroup * kGroup];
-  quant_dual_tile(x, ldx, qr, ldqr, sr, ld_sr, qc, ldqc, sc, ld_sc, blockIdx.x, blockIdx.y, red, tile);
+  // Bands of 128 rows go out last-first, so the first rows' codes are the last written and the
+  // likeliest to be cached when a weight gradient starts its reduction over the rows from the
+  // first (interleaved A/B on dY of the gate+up layer step, 15 rounds: wgrad 1.4 us faster, in
+  // 14 of them; the step 1.8 us).
+  quant_dual_tile(x, ldx, qr, ldqr, sr, ld_sr, qc, ldqc, sc, ld_sc, blockIdx.x, gridDim.y - 1 - blockIdx.y, red, tile);
 }
 
 // ---------------------------------------------------------------------------------------------
